@@ -1,0 +1,357 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is checked against things other than itself: values printed on the
+pages (tests/golden/*.json, each citing its page and section), closed forms,
+invariants, central finite differences and library routines (torch's fp64
+softmax / scaled_dot_product_attention / autograd).  Each group is chosen so a
+plausible slip in the oracle -- a dropped alpha, a wrong sign in dS, a
+transposed operand, a wrong mask offset -- fails at least one test.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import (attention_backward, attention_forward, attention_forward_rows,
+                    online_rescale, softmax, tiled_forward,
+                    tiled_forward_renormalised, visible_mask)
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- page pins
+def test_p4_worked_row_plain_and_tiled(golden):
+    g = golden("p4_tiled_row.json")
+    tol = 0.5 * 10.0 ** -g["printed_decimals"]
+    # the row as attention: q = e1, k_j = (score_j, 0), scale 1
+    q = np.array([[1.0, 0.0]])
+    K = np.array([[s, 0.0] for s in g["scores"]])
+    V = np.array(g["values"])
+    O, L = attention_forward(q, K, V, 1.0, False)
+    assert np.max(np.abs(O[0] - g["output"])) <= tol
+    for tile in (1, 2, 3, 4):
+        Ot, Lt = tiled_forward(q, K, V, 1.0, False, 1, tile)
+        assert np.max(np.abs(Ot - O)) <= 1e-12
+        assert abs(Lt[0] - L[0]) <= 1e-12
+        Or, Lr = tiled_forward_renormalised(q, K, V, 1.0, False, 1, tile)
+        assert np.max(np.abs(Or - O)) <= 1e-12
+        assert abs(Lr[0] - L[0]) <= 1e-12
+    # state after the first key block of size 2
+    _, _, tr = tiled_forward(q, K, V, 1.0, False, 1, g["tile"], trace=True)
+    m1, l1, acc1 = tr[0][0]
+    st = g["after_first_block"]
+    assert abs(m1[0] - st["m"]) <= tol
+    assert abs(l1[0] - st["l"]) <= tol
+    assert np.max(np.abs(acc1[0] - st["acc"])) <= tol
+    # LSE from the definition: log sum exp of the scores
+    assert abs(L[0] - math.log(sum(math.exp(s) for s in g["scores"]))) <= 1e-12
+
+
+def test_p2_rescale_numbers(golden):
+    g = golden("p2_rescale.json")
+    tol = g["printed_abs_tol"]
+    m_new, alpha, l_folded = online_rescale(g["m"], g["l"], g["block_max"], 0.0)
+    assert m_new == g["m_new"]
+    assert abs(alpha - g["alpha"]) <= tol["alpha"]
+    assert abs(l_folded - g["l_folded"]) <= tol["l_folded"]
+    assert abs(alpha - math.exp(-2.0)) <= 1e-15
+
+
+def test_p2_rescale_inside_tiled_recurrence(golden):
+    """Drive tiled_forward through the page's state: after a first block of
+    ten scores equal to 3 the state is m=3, l=10; a second block whose max is
+    5 must fold l to 10*alpha before adding its own sum."""
+    g = golden("p2_rescale.json")
+    scores = [3.0] * 10 + [5.0]
+    q = np.array([[1.0]])
+    K = np.array([[s] for s in scores])
+    V = np.ones((11, 1))
+    _, _, tr = tiled_forward(q, K, V, 1.0, False, 1, 10, trace=True)
+    (m1, l1, _), (m2, l2, _) = tr[0]
+    assert m1[0] == g["m"] and abs(l1[0] - g["l"]) <= 1e-12
+    assert m2[0] == g["m_new"]
+    folded = l2[0] - 1.0           # the new block contributes exp(5-5) = 1
+    assert abs(folded - g["l_folded"]) <= g["printed_abs_tol"]["l_folded"]
+    assert abs(folded - 10.0 * math.exp(-2.0)) <= 1e-12
+
+
+def test_p1_softmax_printed_values(golden):
+    g = golden("p1_softmax.json")
+    for case in g["cases"]:
+        x = np.array(case["x"])
+        y = softmax(x)
+        assert np.all(np.isfinite(y))
+        assert np.max(np.abs(y - case["y"])) <= g["printed_abs_tol"]
+        # the same numbers through attention: q = e1, K[:,0] = x, V = I
+        n = x.size
+        q = np.zeros((1, 2)); q[0, 0] = 1.0
+        K = np.zeros((n, 2)); K[:, 0] = x
+        O, L = attention_forward(q, K, np.eye(n), 1.0, False)
+        assert np.max(np.abs(O[0] - case["y"])) <= g["printed_abs_tol"]
+        Ot, _ = tiled_forward(q, K, np.eye(n), 1.0, False, 1, 2)
+        assert np.max(np.abs(Ot[0] - case["y"])) <= g["printed_abs_tol"]
+
+
+def test_p1_attention_row_printed_values(golden):
+    g = golden("p1_attention_row.json")
+    q = np.array([g["q"]])
+    K = np.array(g["K"])
+    V = np.array(g["V"])
+    O, L = attention_forward(q, K, V, 1.0, False)
+    assert np.max(np.abs(O[0] - g["output"])) <= g["printed_abs_tol"]
+    # the per-key 1-pass recurrence is the block-size-1 case
+    O1, L1 = tiled_forward(q, K, V, 1.0, False, 1, 1)
+    assert np.max(np.abs(O1[0] - g["output"])) <= g["printed_abs_tol"]
+    Or, _ = tiled_forward_renormalised(q, K, V, 1.0, False, 1, 1)
+    assert np.max(np.abs(Or[0] - g["output"])) <= g["printed_abs_tol"]
+    logits = K @ q[0]
+    assert abs(L[0] - math.log(np.sum(np.exp(logits)))) <= 1e-12
+
+
+def test_p3_seeded_cases_tiled_equals_plain(golden):
+    g = golden("p3_seeded_cases.json")
+    for c in g["cases"]:
+        torch.manual_seed(c["seed"])
+        q = torch.randn(c["seq"], c["dim"])
+        k = torch.randn(c["seq"], c["dim"])
+        v = torch.randn(c["seq"], c["dim"])
+        scale = 1.0 / math.sqrt(c["dim"])
+        qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+        O, L = attention_forward(qd, kd, vd, scale, False)
+        Ot, Lt = tiled_forward(qd, kd, vd, scale, False, c["block"], c["block"])
+        Or, _ = tiled_forward_renormalised(qd, kd, vd, scale, False, c["block"], c["block"])
+        # library routine in fp64: softmax(q k^T scale) v
+        ref = torch.softmax((q.double() @ k.double().T) * scale, dim=-1) @ v.double()
+        assert np.max(np.abs(O - ref.numpy())) <= 1e-12
+        assert np.max(np.abs(Ot - O)) <= 1e-12
+        assert np.max(np.abs(Or - O)) <= 1e-12
+        assert np.max(np.abs(Lt - L)) <= 1e-12
+        assert np.max(np.abs(O - ref.numpy())) < g["page_threshold"]
+
+
+# ---------------------------------------------------- library-routine checks
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 3, 17, 17, 8), (1, 2, 64, 64, 16), (1, 1, 1, 1, 4)])
+def test_forward_matches_torch_sdpa_fp64(shape, causal):
+    B, H, Nq, Nk, d = shape
+    r = rng(1)
+    q, k, v = (r.standard_normal((B, H, n, d)) for n in (Nq, Nk, Nk))
+    scale = 0.37
+    O, L = attention_forward(q, k, v, scale, causal)
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    s = (tq @ tk.transpose(-1, -2)) * scale
+    if causal:  # Nq == Nk here, so top-left and bottom-right alignment agree
+        s = s.masked_fill(torch.triu(torch.ones(Nq, Nk, dtype=torch.bool), 1), float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    assert np.max(np.abs(O - ref.numpy())) <= 1e-12
+    assert np.max(np.abs(L - lse.numpy())) <= 1e-12
+
+
+def test_bottom_right_alignment_when_nq_ne_nk():
+    # Nq < Nk: the last query sees every key; query i sees Nk - Nq + i + 1 keys
+    m = visible_mask(3, 7, True)
+    assert m.sum(axis=1).tolist() == [5, 6, 7]
+    # Nq > Nk: the first Nq - Nk queries see nothing
+    m = visible_mask(6, 4, True)
+    assert m.sum(axis=1).tolist() == [0, 0, 1, 2, 3, 4]
+    assert visible_mask(5, 5, True).sum() == 15
+    assert visible_mask(5, 9, False).all()
+
+
+# ---------------------------------------------------------------- invariants
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_of_p_sum_to_one(causal):
+    r = rng(2)
+    N, d = 37, 8
+    q, k = r.standard_normal((N, d)) * 3, r.standard_normal((N, d)) * 3
+    P, _ = attention_forward(q, k, np.eye(N), 0.5, causal)   # V = I gives O = P
+    assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= 1e-14
+    if causal:
+        assert np.all(P[visible_mask(N, N, True) == False] == 0.0)  # noqa: E712
+
+
+def test_masked_keys_get_zero_weight_bitwise():
+    r = rng(3)
+    N, d = 29, 8
+    q, k, v = (r.standard_normal((N, d)) for _ in range(3))
+    O, L = attention_forward(q, k, v, 0.3, True)
+    i0 = 11
+    k2, v2 = k.copy(), v.copy()
+    k2[i0 + 1:] = r.standard_normal((N - i0 - 1, d)) * 100
+    v2[i0 + 1:] = 1e6
+    O2, L2 = attention_forward(q, k2, v2, 0.3, True)
+    assert np.array_equal(O[: i0 + 1], O2[: i0 + 1])
+    assert np.array_equal(L[: i0 + 1], L2[: i0 + 1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_and_affine_invariance(causal):
+    r = rng(4)
+    Nq, Nk, d = 19, 23, 8
+    scale = 0.25
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, 5))
+    O, L = attention_forward(q, k, v, scale, causal)
+    u = r.standard_normal(d)
+    O2, L2 = attention_forward(q, k + u, v, scale, causal)
+    live = np.isfinite(L)
+    assert np.max(np.abs(O2 - O)) <= 1e-12
+    assert np.max(np.abs((L2 - L)[live] - scale * (q @ u)[live])) <= 1e-12
+    c = r.standard_normal(5)
+    O3, _ = attention_forward(q, k, v + c, scale, causal)
+    assert np.max(np.abs(O3 - (O + c))) <= 1e-12
+
+
+def test_joint_key_value_permutation_noncausal():
+    r = rng(5)
+    q, k, v = r.standard_normal((9, 4)), r.standard_normal((13, 4)), r.standard_normal((13, 3))
+    perm = r.permutation(13)
+    O, L = attention_forward(q, k, v, 1.0, False)
+    O2, L2 = attention_forward(q, k[perm], v[perm], 1.0, False)
+    assert np.max(np.abs(O - O2)) <= 1e-13 and np.max(np.abs(L - L2)) <= 1e-13
+
+
+# --------------------------------------------------------------- closed forms
+def test_closed_forms():
+    r = rng(6)
+    d = 6
+    q = r.standard_normal((5, d))
+    k1, v1 = r.standard_normal((1, d)), r.standard_normal((1, 3))
+    O, L = attention_forward(q, k1, v1, 0.7, False)
+    assert np.max(np.abs(O - v1)) <= 1e-15
+    assert np.max(np.abs(L - 0.7 * (q @ k1[0]))) <= 1e-15
+    # K = 0: uniform weights over the visible keys
+    N = 12
+    q = r.standard_normal((N, d))
+    v = r.standard_normal((N, 3))
+    O, L = attention_forward(q, np.zeros((N, d)), v, 1.0, True)
+    for i in range(N):
+        assert np.max(np.abs(O[i] - v[: i + 1].mean(axis=0))) <= 1e-14
+        assert abs(L[i] - math.log(i + 1)) <= 1e-14
+    # causal row 0 sees only key 0
+    O, _ = attention_forward(q, r.standard_normal((N, d)), v, 1.0, True)
+    assert np.max(np.abs(O[0] - v[0])) <= 1e-15
+
+
+def test_empty_rows_when_nq_exceeds_nk():
+    r = rng(7)
+    q, k, v = r.standard_normal((6, 4)), r.standard_normal((4, 4)), r.standard_normal((4, 4))
+    O, L = attention_forward(q, k, v, 1.0, True)
+    assert np.all(O[:2] == 0.0) and np.all(np.isneginf(L[:2]))
+    assert np.all(np.isfinite(L[2:]))
+    Ot, Lt = tiled_forward(q, k, v, 1.0, True, 4, 2)
+    assert np.max(np.abs(Ot - O)) <= 1e-12
+    assert np.all(np.isneginf(Lt[:2])) and np.max(np.abs(Lt[2:] - L[2:])) <= 1e-12
+
+
+@pytest.mark.parametrize("bq,bk", [(64, 64), (7, 5), (128, 32), (1, 200)])
+def test_tiled_equals_untiled_ragged(bq, bk):
+    r = rng(8)
+    Nq, Nk, d = 150, 170, 16
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    for causal in (False, True):
+        O, L = attention_forward(q, k, v, 0.25, causal)
+        Ot, Lt = tiled_forward(q, k, v, 0.25, causal, bq, bk)
+        assert np.max(np.abs(Ot - O)) <= 1e-12
+        assert np.max(np.abs(Lt - L)) <= 1e-12
+
+
+def test_row_sampled_forward_agrees():
+    r = rng(9)
+    q, k, v = (r.standard_normal((2, 3, 40, 8)) for _ in range(3))
+    rows = [0, 5, 17, 39]
+    O, L = attention_forward(q, k, v, 0.4, True)
+    Os, Ls = attention_forward_rows(q, k, v, 0.4, True, rows)
+    assert np.array_equal(Os, O[:, :, rows]) and np.array_equal(Ls, L[:, :, rows])
+
+
+def test_large_logits_do_not_overflow():
+    q = np.zeros((1, 2)); q[0, 0] = 1.0
+    K = np.zeros((3, 2)); K[:, 0] = [1000.0, 1001.0, 1002.0]
+    O, L = attention_forward(q, K, np.eye(3), 1.0, False)
+    assert np.all(np.isfinite(O)) and np.isfinite(L[0])
+    assert abs(L[0] - (1002.0 + math.log(1 + math.exp(-1) + math.exp(-2)))) <= 1e-12
+
+
+# ------------------------------------------------------------------ backward
+def _loss(q, k, v, do, scale, causal):
+    O, _ = attention_forward(q, k, v, scale, causal)
+    return float(np.sum(O * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(5, 7, 3, 2), (6, 4, 4, 4), (8, 8, 2, 3)])
+def test_backward_finite_differences(shape, causal):
+    Nq, Nk, d, dv = shape
+    r = rng(10)
+    q, k = r.standard_normal((Nq, d)), r.standard_normal((Nk, d))
+    v, do = r.standard_normal((Nk, dv)), r.standard_normal((Nq, dv))
+    scale = 0.6
+    dq, dk, dvv, *_ = attention_backward(q, k, v, do, scale, causal)
+    h = 1e-6
+    for X, G in ((q, dq), (k, dk), (v, dvv)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(*X.shape):
+            old = X[idx]
+            X[idx] = old + h
+            fp = _loss(q, k, v, do, scale, causal)
+            X[idx] = old - h
+            fm = _loss(q, k, v, do, scale, causal)
+            X[idx] = old
+            num[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(num - G)) <= 1e-7 * max(1.0, np.max(np.abs(G)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd_fp64(causal):
+    r = rng(11)
+    B, H, N, d = 2, 2, 33, 8
+    q, k, v, do = (r.standard_normal((B, H, N, d)) for _ in range(4))
+    scale = 1 / math.sqrt(d)
+    dq, dk, dvv, O, L, D = attention_backward(q, k, v, do, scale, causal)
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    s = (tq @ tk.transpose(-1, -2)) * scale
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    out = torch.softmax(s, dim=-1) @ tv
+    out.backward(torch.from_numpy(do))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dvv, tv.grad)):
+        assert np.max(np.abs(mine - ref.numpy())) <= 1e-12
+    assert np.max(np.abs(O - out.detach().numpy())) <= 1e-12
+    assert np.max(np.abs(D - np.sum(do * O, axis=-1))) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    r = rng(12)
+    Nq, Nk, d = 21, 21, 6
+    q, k, v, do = (r.standard_normal((n, d)) for n in (Nq, Nk, Nk, Nq))
+    dq, dk, dvv, *_ = attention_backward(q, k, v, do, 0.5, causal)
+    assert np.max(np.abs(dk.sum(axis=0))) <= 1e-12          # rows of dS sum to 0
+    assert np.max(np.abs(dvv.sum(axis=0) - do.sum(axis=0))) <= 1e-12
+    u = r.standard_normal(d)
+    dq2, *_ = attention_backward(q, k + u, v, do, 0.5, causal)
+    assert np.max(np.abs(dq2 - dq)) <= 1e-12
+
+
+def test_backward_empty_rows_contribute_nothing():
+    r = rng(13)
+    q, do = r.standard_normal((6, 4)), r.standard_normal((6, 4))
+    k, v = r.standard_normal((4, 4)), r.standard_normal((4, 4))
+    dq, dk, dvv, *_ = attention_backward(q, k, v, do, 1.0, True)
+    assert np.all(dq[:2] == 0.0)
+    do2 = do.copy(); do2[:2] = 123.0
+    q2 = q.copy(); q2[:2] = -50.0
+    _, dk2, dv2, *_ = attention_backward(q2, k, v, do2, 1.0, True)
+    assert np.array_equal(dk, dk2) and np.array_equal(dvv, dv2)
+
+
+def test_flop_count_matches_mask():
+    for (Nq, Nk, causal) in [(64, 64, True), (30, 70, True), (70, 30, True), (33, 65, False)]:
+        pairs = int(visible_mask(Nq, Nk, causal).sum())
+        assert oracle.attention_flops(2, 3, Nq, Nk, 16, causal) == 4 * 16 * pairs * 6
