@@ -1,0 +1,179 @@
+"""MI355X-native exact attention: Python binding of the C-ABI library libfa.so.
+
+The binding only marshals arguments.  Every step of the attention forward and
+backward runs in the HIP kernels of ``libfa.so`` (built from ``csrc/`` for
+gfx950); PyTorch supplies device memory and the current stream.  If the
+library is missing, every call raises -- there is no fallback path.
+
+Raw entry points, same names and argument order as ``include/fa.h``:
+    fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, stream) -> int
+    fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal,
+           dtype, workspace, workspace_bytes, stream) -> int
+    fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) -> int
+    fa_strerror(status) -> str
+(pointer arguments are integers: device addresses, 0 for NULL)
+
+Tensor helpers that allocate the outputs with torch and raise ``FAError`` on a
+non-zero status:
+    attention_forward(q, k, v, scale=None, causal=False) -> (o, lse)
+    attention_backward(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FA_F32", "FA_BF16", "FAError", "library_path", "load_library",
+    "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror",
+    "attention_forward", "attention_backward",
+]
+
+FA_F32 = 0
+FA_BF16 = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where} failed with status {status}: {fa_strerror(status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libfa.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfa.so from the package directory (built in-tree); raise if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_attention_20_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _p(x):
+    return None if not x else ctypes.c_void_p(int(x))
+
+
+def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, stream) -> int:
+    return load_library().fa_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Nq, Nk, d,
+                                 float(scale), int(causal), int(dtype), _p(stream))
+
+
+def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype,
+           workspace, workspace_bytes, stream) -> int:
+    return load_library().fa_bwd(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq), _p(dk),
+                                 _p(dv), B, H, Nq, Nk, d, float(scale), int(causal), int(dtype),
+                                 _p(workspace), int(workspace_bytes), _p(stream))
+
+
+def fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype))
+
+
+def fa_strerror(status: int) -> str:
+    return load_library().fa_strerror(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# torch tensor helpers (memory and stream plumbing only)
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _check(t, name, shape, dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def attention_forward(q, k, v, scale=None, causal=False, out=None, lse=None, want_lse=True):
+    """O = softmax(scale * q k^T) v and the natural-log LSE, via fa_fwd.
+
+    q [B,H,Nq,d], k and v [B,H,Nk,d]; bf16 or fp32; contiguous; on the GPU.
+    Returns (o, lse); lse is None when want_lse is False and none is given.
+    """
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dt = q.dtype
+    _check(q, "q", (B, H, Nq, d), dt)
+    _check(k, "k", (B, H, Nk, d), dt)
+    _check(v, "v", (B, H, Nk, d), dt)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", (B, H, Nq, d), dt)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", (B, H, Nq), torch.float32)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                lse.data_ptr() if lse is not None else 0, B, H, Nq, Nk, d, scale,
+                causal, _dtype_code(q), _stream())
+    if st != 0:
+        raise FAError(st, "fa_fwd")
+    return out, lse
+
+
+def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
+    """dq, dk, dv of sum(do * o) via fa_bwd (bf16 only).  ``o`` and ``lse``
+    are the outputs of ``attention_forward`` for the same inputs."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dt = q.dtype
+    for t, n, s in ((q, "q", (B, H, Nq, d)), (k, "k", (B, H, Nk, d)), (v, "v", (B, H, Nk, d)),
+                    (o, "o", (B, H, Nq, d)), (do, "do", (B, H, Nq, d))):
+        _check(t, n, s, dt)
+    _check(lse, "lse", (B, H, Nq), torch.float32)
+    code = _dtype_code(q)
+    need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d,
+                scale, causal, code, workspace.data_ptr() if workspace is not None else 0,
+                workspace.numel() if workspace is not None else 0, _stream())
+    if st != 0:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

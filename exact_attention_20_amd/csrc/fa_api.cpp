@@ -1,0 +1,125 @@
+// C ABI entry points declared in include/fa.h: argument validation, variant
+// dispatch and launch on the caller's stream.  Validation runs before any HIP
+// call, so a rejected call enqueues nothing and touches no output.
+#include "fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Shared checks of sizes, head dim, dtype and scale.
+int check_common(int B, int H, int Nq, int Nk, int d, float scale, int dtype) {
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+    if (Nq > FA_MAX_SEQ || Nk > FA_MAX_SEQ) return FA_ERR_SHAPE;
+    // every element index must fit in int64 and the grid in 32 bits
+    const long double elems = (long double)B * H * (long double)(Nq > Nk ? Nq : Nk) * 128.0L;
+    if (elems > 4.0e18L) return FA_ERR_SHAPE;
+    if ((long double)B * H * ((Nq + 63) / 64 + 1) > 2.0e9L) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    return FA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      int dtype, void* stream) {
+    int st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    const long BH = (long)B * H;
+    if (BH == 0 || Nq == 0) return FA_OK;
+    if (!q || !o || (Nk > 0 && (!k || !v))) return FA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(o) || (Nk > 0 && (!aligned16(k) || !aligned16(v)))) return FA_ERR_ALIGN;
+    if (lse && !aligned4(lse)) return FA_ERR_ALIGN;
+
+    const int br = fa::fwd_rows_per_workgroup(dtype, d);
+    const int n_qtiles = (Nq + br - 1) / br;
+    fa::FwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.n_qtiles = n_qtiles;
+    p.total_wg = (int)(BH * n_qtiles);
+    p.scale_log2 = scale * 1.44269504088896340736f;
+    return hip_status(fa::launch_fwd(dtype, d, causal != 0, (int)BH, p, (hipStream_t)stream));
+}
+
+extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
+    if (check_common(B, H, Nq, Nk, d, 1.0f, dtype) != FA_OK) return 0;
+    if (dtype != FA_BF16) return 0;
+    const size_t rows = (size_t)B * H * Nq;
+    size_t acc = rows * d * sizeof(float);
+    acc = (acc + 255) & ~(size_t)255;
+    size_t vec = rows * sizeof(float);
+    vec = (vec + 255) & ~(size_t)255;
+    return acc + vec;
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    const long BH = (long)B * H;
+    if (BH == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
+    const bool has_q = Nq > 0, has_k = Nk > 0;
+    if ((has_q && (!q || !o || !lse || !dO || !dq)) || (has_k && (!k || !v || !dk || !dv))) return FA_ERR_NULL;
+    if (has_q && (!aligned16(q) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) || !aligned4(lse)))
+        return FA_ERR_ALIGN;
+    if (has_k && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))) return FA_ERR_ALIGN;
+    const size_t need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
+
+    const size_t rows = (size_t)BH * Nq;
+    size_t acc_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+    fa::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.dO = dO;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dq_acc = (float*)workspace;
+    p.dvec = (float*)((char*)workspace + acc_bytes);
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.BH = (int)BH;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.44269504088896340736f;
+    return hip_status(fa::launch_bwd(d, causal != 0, p, (hipStream_t)stream));
+}
+
+extern "C" const char* fa_strerror(int status) {
+    switch (status) {
+        case FA_OK: return "success";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "negative size or sizes beyond the supported limits";
+        case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
+        case FA_ERR_DTYPE: return "unsupported dtype for this call";
+        case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned (lse: 4-byte)";
+        case FA_ERR_WORKSPACE: return "workspace is NULL or smaller than fa_bwd_workspace_bytes()";
+        case FA_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+        case FA_ERR_SCALE: return "scale must be finite and > 0";
+        default: return "unknown status";
+    }
+}

@@ -1,0 +1,101 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// vector types, the 32x32 MFMA wrappers, LDS tile swizzles, and the
+// register-level 4x8 bf16 transpose used to stage a tile key-major.
+//
+// MFMA register layouts used throughout (CDNA3/CDNA4 32x32 shapes, wave64):
+//   A operand (M x K):  lane l holds row m = l % 32, k-group l / 32.
+//   B operand (K x N):  lane l holds col n = l % 32, k-group l / 32.
+//   C/D (M x N, 16 f32 per lane): item t of lane l is
+//       row m = (t / 4) * 8 + (l / 32) * 4 + (t % 4),  col n = l % 32.
+// Only the A/B agreement on which (lane-group, slot) meets which k matters
+// for a product, so every operand pair below is loaded with one mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// 2^x on the hardware transcendental unit (v_exp_f32): -inf -> 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Byte offset of 16-byte chunk `chunk` of row `row` in a row-major LDS tile
+// whose rows are `row_bytes` long.  The chunk index is XOR-ed with the low
+// three bits of the row, so eight consecutive rows read at the same logical
+// chunk land in eight different bank groups (conflict-free ds_read_b128).
+// Rows shorter than 8 chunks XOR with fewer bits so the chunk stays in its row.
+template <uint32_t ROW_BYTES>
+__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
+    constexpr uint32_t kChunks = ROW_BYTES / 16;
+    constexpr uint32_t kMask = kChunks >= 8 ? 7u : kChunks - 1u;
+    static_assert(ROW_BYTES % 16 == 0 && kChunks >= 1, "rows are whole 16-byte chunks");
+    return row * ROW_BYTES + ((chunk ^ (row & kMask)) << 4);
+}
+
+// Position of index `i` inside its 16-group when a tile is stored
+// "k-permuted": bits 2 and 3 are swapped, so the 8 indices a 32x32x16 MFMA
+// lane-group consumes -- {4g..4g+3, 8+4g..8+4g+3} for g = 0, 1, which is the
+// order a 32x32 accumulator hands them out -- sit in 16 contiguous bytes.
+__device__ __forceinline__ uint32_t kperm(uint32_t i) {
+    return (i & ~12u) | ((i & 4u) << 1) | ((i & 8u) >> 1);
+}
+
+// Transpose four rows x eight bf16 columns held as four 16-byte vectors into
+// eight columns x four rows (each 8 bytes): out[c] = {r0[c], r1[c], r2[c], r3[c]}.
+__device__ __forceinline__ void transpose4x8(const u32x4 (&r)[4], u32x2 (&out)[8]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        // low halves -> column 2p, high halves -> column 2p+1
+        out[2 * p][0] = __builtin_amdgcn_perm(r[1][p], r[0][p], 0x05040100u);
+        out[2 * p][1] = __builtin_amdgcn_perm(r[3][p], r[2][p], 0x05040100u);
+        out[2 * p + 1][0] = __builtin_amdgcn_perm(r[1][p], r[0][p], 0x07060302u);
+        out[2 * p + 1][1] = __builtin_amdgcn_perm(r[3][p], r[2][p], 0x07060302u);
+    }
+}
+
+__device__ __forceinline__ u32x4 ldg128(const void* p) { return *(const u32x4*)p; }
+
+__device__ __forceinline__ u32x4 zero_u32x4() {
+    u32x4 z;
+    z[0] = z[1] = z[2] = z[3] = 0u;
+    return z;
+}
+
+}  // namespace fa

@@ -1,0 +1,405 @@
+// Fused attention forward for gfx950 (MI355X): the FA2-order tiled forward
+// ("01 · IO-awareness、online softmax 与 tiling" §2-§4; "FlashAttention 1～4
+// 全解汇总", FlashAttention-2 algorithm) written for CDNA4 wave64 + MFMA.
+//
+// One workgroup owns one (batch*head, query tile).  Each wave owns 32 query
+// rows of the tile (split over queries, so no cross-wave reduction).  Key /
+// value tiles stream through LDS, double-buffered; S and P never leave the
+// chip.
+//
+// Register-level formulation (bf16 path, 32x32x16 MFMA):
+//   S^T[key][q] = K Q^T    : A = K rows from LDS, B = this wave's Q held in
+//                            VGPRs, so each lane ends up owning ONE query
+//                            (column l%32) and 16 of its keys per 32-key block.
+//   row max / row sum      : lane-local over the 16*NKB values, then one
+//                            exchange with the other 32-lane half.
+//   O^T[dv][q] += V^T P^T  : B = P^T straight from the S^T accumulator (no
+//                            LDS round trip), A = V^T rows from an LDS copy
+//                            of V stored dv-major with keys in the order the
+//                            accumulator hands them out (see kperm).
+//   The rescale by alpha = 2^(m_old - m_new) is a per-lane scalar because a
+//   lane's O^T items all belong to its one query.
+// exp is computed as exp2 with scale*log2(e) folded into one FMA (§4 of the
+// IO-awareness page); LSE is converted back to natural-log units at the end.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+// Workgroup id -> (batch*head, query tile).  MI300-class parts hand
+// consecutive workgroup ids to the 8 XCDs round robin, so ids are regrouped
+// to give each XCD a contiguous run of heads (their K/V then share that
+// XCD's L2).  Within a head the heaviest (last, for causal) query tile is
+// issued first so the short tiles fill the tail.
+__device__ __forceinline__ void map_workgroup(int w, int total, int n_qtiles, int& bh, int& qt) {
+    int L = w;
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        L = (w & 7) * per + (w >> 3);
+    }
+    bh = L / n_qtiles;
+    qt = n_qtiles - 1 - (L - bh * n_qtiles);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 inputs, bf16 output, fp32 accumulation.  BR = 128 (4 waves x 32 rows),
+// BC = 64 keys per tile.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
+    constexpr int BR = 128, BC = 64;
+    constexpr int NKK = D / 16;        // k-steps over d for S^T
+    constexpr int NKB = BC / 32;       // 32-key blocks per tile
+    constexpr int NDB = D / 32;        // 32-row blocks of O^T
+    constexpr int NKC = BC / 16;       // 16-key k-steps for O^T += V^T P^T
+    constexpr int K_BYTES = BC * D * 2;
+    constexpr int BUF_BYTES = 2 * K_BYTES;          // K tile + V^T tile
+    constexpr int KCH = BC * D / 8 / 256;           // 16 B chunks of K per thread
+    constexpr int VUN = (BC / 4) * (D / 8);         // 4-key x 8-dv units of V
+    constexpr int VPT = (VUN + 255) / 256;
+    static_assert(KCH >= 1 && BC * D / 8 % 256 == 0, "K tile must split evenly");
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hg = lane >> 5;
+    int bh, qt;
+    map_workgroup(blockIdx.x, p.total_wg, p.n_qtiles, bh, qt);
+    const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+    const int q0 = qt * BR;
+    const int qw = q0 + wave * 32;     // this wave's first query
+    const int qi = qw + l32;           // this lane's query
+    const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
+    const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
+    const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
+
+    // Key range this workgroup needs: causal stops after the last key the
+    // tile's last query can see; tiles beyond are skipped entirely.
+    const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
+    const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
+    const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;   // same, per wave
+
+    bf16x8 qreg[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 t = zero_u32x4();
+        if (qi < Nq) t = ldg128(Qh + (size_t)qi * D + 16 * kk + 8 * hg);
+        qreg[kk] = __builtin_bit_cast(bf16x8, t);
+    }
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = zero16();
+    float m_run = -INFINITY;   // running max of scale*log2e*S for this lane's query
+    float l_run = 0.f;         // partial running sum over this lane's keys
+
+    u32x4 kst[KCH];
+    u32x4 vst[VPT][4];
+
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + 256 * i, r = c / (D / 8), cc = c % (D / 8);
+            kst[i] = (k0 + r < Nk) ? ldg128(Kh + (size_t)(k0 + r) * D + cc * 8) : zero_u32x4();
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int unit = tid + 256 * u;
+            if (unit < VUN) {
+                const int kg = unit / (D / 8), dc = unit % (D / 8);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int key = k0 + 4 * kg + j;
+                    vst[u][j] = key < Nk ? ldg128(Vh + (size_t)key * D + dc * 8) : zero_u32x4();
+                }
+            }
+        }
+    };
+    auto store_tile = [&](char* buf) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + 256 * i, r = c / (D / 8), cc = c % (D / 8);
+            *(u32x4*)(buf + swz<D * 2>(r, cc)) = kst[i];
+        }
+        char* vt = buf + K_BYTES;
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int unit = tid + 256 * u;
+            if (unit < VUN) {
+                const int kg = unit / (D / 8), dc = unit % (D / 8);
+                u32x2 cols[8];
+                transpose4x8(vst[u], cols);
+                const uint32_t pos = (kg >> 2) * 16 + kperm((kg & 3) * 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t row = dc * 8 + e;
+                    *(u32x2*)(vt + swz<BC * 2>(row, pos >> 3) + (pos & 4u) * 2) = cols[e];
+                }
+            }
+        }
+    };
+
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(smem);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int k0 = t * BC;
+        const char* kbuf = smem + (t & 1) * BUF_BYTES;
+        const char* vtbuf = kbuf + K_BYTES;
+        const bool has_next = t + 1 < ntiles;
+        if (has_next) load_tile(k0 + BC);
+
+        if (k0 < kend_w) {
+            // ---- S^T = K Q^T (fp32 accumulators) ----
+            f32x16 s[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const bf16x8 a = *(const bf16x8*)(kbuf + swz<D * 2>(kb * 32 + l32, 2 * kk + hg));
+                    s[kb] = mfma_bf16(a, qreg[kk], s[kb]);
+                }
+            }
+            // ---- mask: only tiles that straddle the diagonal or the tail ----
+            const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw + off);
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = k0 + kb * 32 + (i >> 2) * 8 + 4 * hg + (i & 3);
+                        const bool vis = key < Nk && (!CAUSAL || key <= qi + off);
+                        if (!vis) s[kb][i] = -INFINITY;
+                    }
+            }
+            // ---- online softmax update (base-2, scale folded) ----
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx * p.scale_log2);
+            // a row with no visible key so far keeps base 0: every term is 0
+            const float base = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = exp2_hw(m_run - base);
+            float rs = 0.f;
+            u32x4 pw[NKC];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float p0 = exp2_hw(fmaf(s[kb][i], p.scale_log2, -base));
+                    const float p1 = exp2_hw(fmaf(s[kb][i + 1], p.scale_log2, -base));
+                    rs += p0 + p1;
+                    pw[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+                }
+            }
+            bf16x8 pb[NKC];
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) pb[kc] = __builtin_bit_cast(bf16x8, pw[kc]);
+            l_run = alpha * l_run + rs;
+            m_run = m_new;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            // ---- O^T += V^T P^T ----
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const bf16x8 a = *(const bf16x8*)(vtbuf + swz<BC * 2>(db * 32 + l32, 2 * kc + hg));
+                    oacc[db] = mfma_bf16(a, pb[kc], oacc[db]);
+                }
+            }
+        }
+
+        if (has_next) store_tile(smem + ((t + 1) & 1) * BUF_BYTES);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l) ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qi < Nq) {
+        bf16* Oh = (bf16*)p.o + (size_t)bh * Nq * D + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+                w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                *(u32x2*)(Oh + db * 32 + g * 8 + 4 * hg) = w;
+            }
+        if (hg == 0 && p.lse)
+            p.lse[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs and output: true fp32 products on the 32x32x2 fp32 MFMA.
+// BR = BC = 64 (2 waves x 32 rows); single-buffered LDS.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(128) fwd_f32_kernel(FwdParams p) {
+    constexpr int BR = 64, BC = D == 128 ? 32 : 64;   // LDS: K (padded) + V within 64 KiB
+    constexpr int NKB = BC / 32, NDB = D / 32;
+    constexpr int KS = D + 1;          // padded K row: lanes on 32 rows hit 32 banks
+    __shared__ float ks[BC * KS];
+    __shared__ __attribute__((aligned(16))) float vs[BC * D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hg = lane >> 5;
+    int bh, qt;
+    map_workgroup(blockIdx.x, p.total_wg, p.n_qtiles, bh, qt);
+    const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+    const int q0 = qt * BR;
+    const int qw = q0 + wave * 32;
+    const int qi = qw + l32;
+    const float* Qh = (const float*)p.q + (size_t)bh * Nq * D;
+    const float* Kh = (const float*)p.k + (size_t)bh * Nk * D;
+    const float* Vh = (const float*)p.v + (size_t)bh * Nk * D;
+
+    const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
+    const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
+    const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
+
+    float qreg[D / 2];
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) qreg[kk] = qi < Nq ? Qh[(size_t)qi * D + 2 * kk + hg] : 0.f;
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = zero16();
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int k0 = t * BC;
+        __syncthreads();
+        for (int c = tid; c < BC * D / 4; c += 128) {
+            const int r = c / (D / 4), cc = c % (D / 4);
+            f32x4 kv, vv;
+            if (k0 + r < Nk) {
+                kv = *(const f32x4*)(Kh + (size_t)(k0 + r) * D + cc * 4);
+                vv = *(const f32x4*)(Vh + (size_t)(k0 + r) * D + cc * 4);
+            } else {
+                kv[0] = kv[1] = kv[2] = kv[3] = 0.f;
+                vv = kv;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ks[r * KS + cc * 4 + e] = kv[e];
+            *(f32x4*)(vs + r * D + cc * 4) = vv;
+        }
+        __syncthreads();
+        if (k0 >= kend_w) continue;
+
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < D / 2; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                s[kb] = mfma_f32(ks[(kb * 32 + l32) * KS + 2 * kk + hg], qreg[kk], s[kb]);
+
+        const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw + off);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + kb * 32 + (i >> 2) * 8 + 4 * hg + (i & 3);
+                    const bool vis = key < Nk && (!CAUSAL || key <= qi + off);
+                    if (!vis) s[kb][i] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx * p.scale_log2);
+        const float base = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2_hw(m_run - base);
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[kb][i] = exp2_hw(fmaf(s[kb][i], p.scale_log2, -base));
+                rs += s[kb][i];
+            }
+        l_run = alpha * l_run + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        // O^T += V^T P^T, two keys (one per 32-lane half) per MFMA
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = kb * 32 + (i >> 2) * 8 + 4 * hg + (i & 3);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] = mfma_f32(vs[key * D + db * 32 + l32], s[kb][i], oacc[db]);
+            }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qi < Nq) {
+        float* Oh = (float*)p.o + (size_t)bh * Nq * D + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * g + e] * inv;
+                *(f32x4*)(Oh + db * 32 + g * 8 + 4 * hg) = w;
+            }
+        if (hg == 0 && p.lse)
+            p.lse[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+int fwd_rows_per_workgroup(int dtype, int d) {
+    (void)d;
+    return dtype == 0 ? 64 : 128;
+}
+
+template <typename KernelT>
+static hipError_t launch(KernelT kernel, int grid, int block, const FwdParams& p, hipStream_t s) {
+    FwdParams pp = p;
+    void* args[] = {&pp};
+    return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(block), args, 0, s);
+}
+
+hipError_t launch_fwd(int dtype, int d, bool causal, int BH, FwdParams p, hipStream_t stream) {
+    const int grid = p.total_wg;
+    (void)BH;
+    if (grid == 0) return hipSuccess;
+    if (dtype == 1) {
+        if (d == 64) return causal ? launch(fwd_bf16_kernel<64, true>, grid, 256, p, stream)
+                                   : launch(fwd_bf16_kernel<64, false>, grid, 256, p, stream);
+        return causal ? launch(fwd_bf16_kernel<128, true>, grid, 256, p, stream)
+                      : launch(fwd_bf16_kernel<128, false>, grid, 256, p, stream);
+    }
+    if (d == 64) return causal ? launch(fwd_f32_kernel<64, true>, grid, 128, p, stream)
+                               : launch(fwd_f32_kernel<64, false>, grid, 128, p, stream);
+    return causal ? launch(fwd_f32_kernel<128, true>, grid, 128, p, stream)
+                  : launch(fwd_f32_kernel<128, false>, grid, 128, p, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,128 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
+ *
+ * Exact scaled-dot-product attention, computed tile by tile with the online
+ * softmax so that the Nq x Nk score matrix S and probability matrix P never
+ * reach device memory:
+ *
+ *     S = scale * Q K^T,   P = row-softmax(S),   O = P V,
+ *     LSE_i = m_i + ln(l_i)  (row max m, row sum l = sum_j exp(S_ij - m_i)).
+ *
+ * Pages defining the operations (cited by title and section):
+ *   "01 · IO-awareness、online softmax 与 tiling": §1 (the three-step
+ *       definition), §2 (online softmax state m, l, O and its rescale),
+ *       §3 (tiled forward: one kernel instance per query tile, loop over key
+ *       tiles, deferred normalisation, LSE saved), §5 (backward by
+ *       recomputation from LSE and its gradient formulas).
+ *   "FlashAttention 1～4 全解汇总": FlashAttention-2 algorithm (parallel over
+ *       query row blocks, O_i = O~_i / l_i, L_i = m_i + log l_i).
+ *   "让注意力计算留在片上：分块 Softmax 的计算与访存分析": §02 (the m, l, u
+ *       recurrence), §04 (recompute P from the saved L in backward).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout   q, o, dO, dq: [B, H, Nq, d];  k, v, dk, dv: [B, H, Nk, d];
+ *          lse: [B, H, Nq].  All contiguous, row-major, d innermost.
+ * dtype    q, k, v, o, dO, dq, dk, dv share `dtype` (FA_F32 or FA_BF16);
+ *          lse is always float32; all accumulation is float32; bf16 results
+ *          are rounded to nearest even.
+ * d        64 or 128.
+ * scale    multiplies the logits (S = scale * Q K^T); must be finite and > 0.
+ *          Usually 1/sqrt(d).
+ * causal   nonzero: key j is visible to query i iff j <= i + (Nk - Nq)
+ *          (bottom-right alignment; j <= i when Nq == Nk).  A query row with
+ *          no visible key gets O = 0 and LSE = -inf and contributes nothing
+ *          to the gradients.
+ * Memory   the caller owns all device memory.  The library allocates nothing,
+ *          frees nothing and keeps no pointer after returning.  Pointers to
+ *          tensors must be 16-byte aligned device pointers; lse 4-byte aligned.
+ * Streams  `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *          enqueued asynchronously; no host synchronisation happens.  Faults
+ *          inside a kernel surface at the caller's next synchronisation.
+ * Errors   0 on success, a negative fa_status_t otherwise.  Arguments are
+ *          validated before any HIP call; on a validation error nothing is
+ *          enqueued and outputs are untouched.  The entry points are
+ *          stateless and may be called from several host threads.
+ * Empty    B, H or Nq equal to 0 is a no-op that returns FA_OK (pointers may
+ *          then be NULL).  Nk == 0 is valid: every row is empty.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_F32 = 0,
+    FA_BF16 = 1
+} fa_dtype_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,       /* a required pointer is NULL                    */
+    FA_ERR_SHAPE = -2,      /* negative size, or sizes beyond the limits     */
+    FA_ERR_HEAD_DIM = -3,   /* d is not 64 or 128                            */
+    FA_ERR_DTYPE = -4,      /* unknown dtype, or one this call does not take */
+    FA_ERR_ALIGN = -5,      /* a tensor pointer is not 16-byte aligned       */
+    FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required       */
+    FA_ERR_LAUNCH = -7,     /* the HIP runtime refused a kernel launch       */
+    FA_ERR_SCALE = -8       /* scale is not finite or not > 0                */
+} fa_status_t;
+
+/* Largest Nq or Nk accepted (keeps every in-head index within 32 bits). */
+#define FA_MAX_SEQ (1 << 24)
+
+/*
+ * Forward pass ("01 · IO-awareness、online softmax 与 tiling" §3;
+ * "FlashAttention 1～4 全解汇总", FlashAttention-2 algorithm).
+ *
+ *   in : q [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,d]          (dtype)
+ *   out: o [B,H,Nq,d] (dtype), lse [B,H,Nq] (float32, natural log)
+ *
+ * lse may be NULL, in which case it is not written.  o must not alias q, k
+ * or v.  Deterministic: the same inputs give bitwise the same outputs.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (float32 dQ
+ * accumulator [B,H,Nq,d] plus the float32 row vector D = rowsum(dO * O)
+ * [B,H,Nq]), rounded up to 256.  Returns 0 for invalid sizes or dtype.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
+
+/*
+ * Backward pass by recomputation ("01 · IO-awareness、online softmax 与
+ * tiling" §5; "让注意力计算留在片上" §04):
+ *
+ *   P = exp(scale * Q K^T - LSE),  dV = P^T dO,  dP = dO V^T,
+ *   D = rowsum(dO * O),  dS = P * (dP - D),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ *   in : q, k, v, o (the forward output), lse (the forward LSE), dO
+ *   out: dq [B,H,Nq,d], dk [B,H,Nk,d], dv [B,H,Nk,d]           (dtype)
+ *   workspace: device memory of at least fa_bwd_workspace_bytes(); its
+ *   contents on entry are ignored and on exit are unspecified.
+ *
+ * Only FA_BF16 is accepted (FA_ERR_DTYPE otherwise).  dq is summed over key
+ * tiles with float32 atomics, so it is not bitwise reproducible run to run;
+ * dk and dv are.  Calls that share a workspace must not overlap.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dO, void* dq, void* dk, void* dv,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* A static, human-readable description of a status code. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

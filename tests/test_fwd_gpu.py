@@ -1,0 +1,216 @@
+"""GPU parity of fa_fwd against the fp64 oracle (MI355X only).
+
+Every case calls the HIP path through the C ABI (exact_attention_20_amd ->
+libfa.so) and compares with the oracle on the same seeded inputs.  Full-size
+workloads run on the GPU at their real shape and launch configuration; the
+oracle then checks sampled heads or rows it can compute one by one.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_20_amd as fa
+import workloads as wl
+from oracle import attention_forward, attention_forward_rows
+from parity import check_forward, to64
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def gpu_fwd(q, k, v, scale, causal):
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = fa.attention_forward(qd, kd, vd, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ------------------------------------------------------------ small / ragged
+SMALL = [
+    # B, H, Nq, Nk, d, dtype, causal
+    (1, 1, 1, 1, 64, "bf16", False),
+    (1, 1, 1, 1, 128, "fp32", True),
+    (2, 3, 17, 17, 64, "bf16", True),
+    (1, 2, 100, 257, 128, "bf16", False),
+    (1, 2, 100, 257, 128, "bf16", True),
+    (1, 2, 257, 100, 128, "bf16", True),      # 157 leading rows see no key
+    (1, 1, 300, 300, 64, "bf16", True),
+    (2, 2, 128, 128, 128, "bf16", True),
+    (1, 1, 129, 64, 64, "bf16", False),
+    (1, 1, 64, 129, 64, "bf16", True),
+    (1, 3, 383, 383, 64, "bf16", False),
+    (1, 2, 77, 130, 64, "fp32", False),
+    (1, 2, 77, 130, 64, "fp32", True),
+    (1, 1, 200, 200, 128, "fp32", True),
+    (1, 1, 200, 71, 128, "fp32", True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_small_and_ragged(case):
+    B, H, Nq, Nk, d, dtype, causal = case
+    banner(f"fwd small {case}")
+    q, k, v = wl.make_inputs(B, H, Nq, Nk, d, dtype, seed=77 + Nq + 3 * Nk + d)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = gpu_fwd(q, k, v, scale, causal)
+    o_ref, lse_ref = attention_forward(to64(q), to64(k), to64(v), scale, causal)
+    check_forward(to64(o), to64(lse), o_ref, lse_ref, dtype, str(case))
+
+
+def test_single_head_fp32_workload():
+    w = wl.SINGLE_HEAD
+    banner(w.describe())
+    q, k, v = wl.workload_inputs(w)
+    o, lse = gpu_fwd(q, k, v, w.scale, w.causal)
+    o_ref, lse_ref = attention_forward(to64(q), to64(k), to64(v), w.scale, w.causal)
+    check_forward(to64(o), to64(lse), o_ref, lse_ref, "fp32", w.name)
+
+
+def _sampled_heads_check(w, n_heads, seed):
+    q, k, v = wl.workload_inputs(w)[:3]
+    o, lse = gpu_fwd(q, k, v, w.scale, w.causal)
+    g = torch.Generator().manual_seed(seed)
+    heads = torch.randperm(w.B * w.H, generator=g)[:n_heads].tolist()
+    for bh in heads:
+        b, h = divmod(bh, w.H)
+        o_ref, lse_ref = attention_forward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), w.scale, w.causal)
+        check_forward(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, w.dtype, f"{w.name} head {bh}")
+
+
+def _sampled_rows_check(w, n_rows, seed):
+    q, k, v = wl.workload_inputs(w)[:3]
+    o, lse = gpu_fwd(q, k, v, w.scale, w.causal)
+    rows = wl.sample_rows(w.Nq, n_rows, seed)
+    o_ref, lse_ref = attention_forward_rows(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                            w.scale, w.causal, rows)
+    check_forward(to64(o[:, :, rows]), to64(lse[:, :, rows]), o_ref, lse_ref, w.dtype, w.name)
+
+
+def test_gpt2_small_workload_sampled_heads():
+    banner(wl.GPT2_SMALL.describe())
+    _sampled_heads_check(wl.GPT2_SMALL, 8, 2002)
+
+
+def test_llama_causal_workload_sampled_rows():
+    banner(wl.LLAMA_CAUSAL.describe())
+    _sampled_rows_check(wl.LLAMA_CAUSAL, 64, 3003)
+
+
+def test_long_context_workload_256_rows_per_head():
+    banner(wl.LONG_CONTEXT.describe())
+    _sampled_rows_check(wl.LONG_CONTEXT, 256, 4004)
+
+
+def test_train_step_forward_sampled_rows():
+    banner(wl.TRAIN_STEP.describe() + " (forward)")
+    _sampled_rows_check(wl.TRAIN_STEP, 96, 5005)
+
+
+# ------------------------------------------------------------------ page pins
+def _pad_fp32(x, width):
+    out = torch.zeros(x.shape[0], width, dtype=torch.float32)
+    out[:, : x.shape[1]] = torch.as_tensor(x, dtype=torch.float32)
+    return out
+
+
+def _pin_run(q, K, V):
+    """One query row through the GPU in fp32 with d zero-padded to 64 (the
+    padding changes neither the logits nor the output columns kept)."""
+    qp = _pad_fp32(np.atleast_2d(q), 64)[None, None]
+    kp = _pad_fp32(K, 64)[None, None]
+    vp = _pad_fp32(V, 64)[None, None]
+    o, lse = gpu_fwd(qp, kp, vp, 1.0, False)
+    return o[0, 0, 0].cpu().double().numpy(), float(lse[0, 0, 0])
+
+
+def test_page_pin_worked_tiled_row():
+    g = json.load(open(os.path.join(GOLDEN, "p4_tiled_row.json")))
+    banner("pin: worked tiled row")
+    K = np.array([[s, 0.0] for s in g["scores"]])
+    o, lse = _pin_run([1.0, 0.0], K, np.array(g["values"]))
+    assert np.max(np.abs(o[:2] - g["output"])) <= 0.5e-6 + 1e-6
+    assert np.all(o[2:] == 0.0)
+    assert abs(lse - np.log(np.sum(np.exp(g["scores"])))) <= 1e-5 * 4
+
+
+def test_page_pin_one_row_attention():
+    g = json.load(open(os.path.join(GOLDEN, "p1_attention_row.json")))
+    banner("pin: one-row attention")
+    o, _ = _pin_run(g["q"], np.array(g["K"]), np.array(g["V"]))
+    assert np.max(np.abs(o[:2] - g["output"])) <= 1e-5 * 2
+
+
+def test_page_pin_softmax_values_including_large_logits():
+    g = json.load(open(os.path.join(GOLDEN, "p1_softmax.json")))
+    for case in g["cases"]:
+        banner(f"pin: softmax {case['x']}")
+        x = np.array(case["x"])
+        n = x.size
+        K = np.zeros((n, 2)); K[:, 0] = x
+        o, lse = _pin_run([1.0, 0.0], K, np.eye(n))
+        assert np.all(np.isfinite(o)) and np.isfinite(lse)
+        assert np.max(np.abs(o[:n] - case["y"])) <= 1e-6
+
+
+# ------------------------------------------------------------ invariants/edges
+def test_no_keys_gives_zero_rows():
+    banner("Nk = 0")
+    q = torch.randn(1, 2, 40, 64).to(torch.bfloat16).cuda()
+    k = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = fa.attention_forward(q, k, k.clone(), causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_masked_keys_do_not_change_rows_bitwise():
+    banner("masked keys perturbation")
+    q, k, v = wl.make_inputs(1, 2, 300, 300, 128, "bf16", seed=99)
+    o1, l1 = gpu_fwd(q, k, v, 0.1, True)
+    i0 = 150
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, i0 + 1:] = torch.randn_like(k2[:, :, i0 + 1:].float()).to(torch.bfloat16) * 8
+    v2[:, :, i0 + 1:] = 100.0
+    o2, l2 = gpu_fwd(q, k2, v2, 0.1, True)
+    assert torch.equal(o1[:, :, : i0 + 1], o2[:, :, : i0 + 1])
+    assert torch.equal(l1[:, :, : i0 + 1], l2[:, :, : i0 + 1])
+
+
+def test_forward_is_deterministic():
+    banner("determinism")
+    q, k, v = wl.make_inputs(2, 4, 500, 500, 128, "bf16", seed=5)
+    o1, l1 = gpu_fwd(q, k, v, 0.088, True)
+    o2, l2 = gpu_fwd(q, k, v, 0.088, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_lse_pointer_may_be_null():
+    banner("lse = NULL")
+    q, k, v = (t.cuda() for t in wl.make_inputs(1, 2, 130, 130, 64, "bf16", seed=6))
+    o_ref, _ = fa.attention_forward(q, k, v, causal=True)
+    o = torch.empty_like(q)
+    st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), 0, 1, 2, 130, 130, 64,
+                   0.125, 1, fa.FA_BF16, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0 and torch.equal(o, o_ref)
+
+
+def test_shift_and_value_offset_invariance_fp32():
+    banner("shift invariance fp32")
+    q, k, v = wl.make_inputs(1, 2, 90, 90, 64, "fp32", seed=8)
+    u = torch.randn(64)
+    o1, l1 = gpu_fwd(q, k, v, 0.2, True)
+    o2, l2 = gpu_fwd(q, k + u, v, 0.2, True)
+    o3, _ = gpu_fwd(q, k, v + 3.0, 0.2, True)
+    assert torch.max(torch.abs(o2 - o1)).item() <= 1e-5
+    shift = 0.2 * (q @ u)
+    assert torch.max(torch.abs((l2 - l1).cpu() - shift)).item() <= 1e-4
+    assert torch.max(torch.abs(o3 - (o1 + 3.0))).item() <= 1e-5
