@@ -1,0 +1,181 @@
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+A step is one fa_fwd launch over the whole workload (default: B=4 H=32
+N=4096 d=128 bf16 causal, LSE saved), with Q, K, V already resident in device
+memory.  W untimed warm-up steps, then K steps timed with HIP events recorded
+on the stream the kernel is launched on, bracketed by device synchronisation.
+Throughput is causal-adjusted: 4*d FLOPs per visible (query, key) pair.
+
+Prints ONE JSON line.  ``roofline`` compares the kernel against MI355X's
+published dense bf16 MFMA peak (2.5 PFLOP/s); ``traffic`` is taken from the
+committed rocprofv3 counter summary when it was measured on the current kernel
+source, else null.  ``cpu_baseline`` times the fp64 oracle on a bounded sample
+of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16, causal-adjusted) and % of MFMA peak, 1×MI355X"
+PEAK = {"bf16": 2500.0, "fp32": 157.3}          # TFLOP/s, MI355X published dense figures
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["exact_attention_20_amd/csrc/fa_fwd.hip", "exact_attention_20_amd/csrc/fa_device.h"]
+
+
+def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
+    """Number of (query, key) pairs the mask leaves visible (bottom-right
+    aligned causal mask: key j visible to query i iff j <= i + Nk - Nq)."""
+    if not causal:
+        return Nq * Nk
+    off = Nk - Nq
+    total = 0
+    for i in range(Nq):
+        total += min(Nk, max(0, i + off + 1))
+    return total
+
+
+def fwd_flops(w) -> int:
+    return 4 * w.d * visible_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload_name: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get("workloads", {}).get(workload_name)
+    if not entry or t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, target_s: float = 15.0):
+    """Time the fp64 oracle (as it stands) on whole heads of the workload until
+    about ``target_s`` seconds of CPU work; report its causal-adjusted rate."""
+    import numpy as np
+    from oracle import attention_forward
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max(blas) if blas else 1
+    except Exception:
+        threads = 1
+    per_head_flops = fwd_flops(w) / (w.B * w.H)
+    done, t_total = 0, 0.0
+    heads = w.B * w.H
+    while done < heads and t_total < target_s:
+        b, h = divmod(done, w.H)
+        qh, kh, vh = (t[b, h].double().numpy() for t in (q, k, v))
+        t0 = time.perf_counter()
+        attention_forward(qh, kh, vh, w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+    rate = per_head_flops * done / t_total / 1e12
+    return {"value": round(rate, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {heads} (batch, head) pairs of {w.describe()}, fp64 NumPy, "
+                      f"{t_total:.1f} s; numpy exp single-threaded, BLAS {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama_causal_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards over batch*head with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_20_amd as fa
+    import workloads as wl
+
+    w = {x.name: x for x in wl.ALL}[args.workload]
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    q, k, v = wl.workload_inputs(w)[:3]
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    dtype_code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+    argv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), dtype_code, sh)
+
+    def step():
+        st = fa.fa_fwd(*argv)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms = ms_total / args.steps
+    flops = fwd_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK[w.dtype]
+
+    traffic = traffic_for(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid N(0,1) inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "lse_saved": True, "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
