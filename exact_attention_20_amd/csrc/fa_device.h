@@ -18,6 +18,7 @@ namespace fa {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -91,6 +92,57 @@ __device__ __forceinline__ void transpose4x8(const u32x4 (&r)[4], u32x2 (&out)[8
 }
 
 __device__ __forceinline__ u32x4 ldg128(const void* p) { return *(const u32x4*)p; }
+
+// Raw buffer resource over `bytes` bytes at `base`.  Loads through it return
+// zero for any 16-byte chunk at or past `bytes`, which is how ragged tails are
+// read without branches.  (Word 3 = 0x00020000: 32-bit raw data format.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16-byte buffer load at byte offset voff (per lane) + soff (uniform).
+__device__ __forceinline__ u32x4 buf_load128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// 16 bytes per lane from a buffer straight into LDS (no VGPRs): lane l's
+// data lands at lds_base + 16*l.  lds_base must be the same in every lane.
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff,
+                                               uint32_t soff) {
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, soff, 0, 0);
+}
+
+// ds_read_b64_tr_b16 (gfx950): inside each 16-lane group, lane i receives
+// element i%4 of the 8 bytes read by lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+    typedef __attribute__((address_space(3))) v4bf lds_v4bf;
+    const v4bf r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 concat8(bf16x4 lo, bf16x4 hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = lo[i];
+        r[i + 4] = hi[i];
+    }
+    return r;
+}
+
+// v_permlane32_swap exchanges the two 32-lane halves; the pair it returns
+// holds {x[l], x[l ^ 32]} in every lane, so max / sum over the pair combine a
+// lane with its partner in the other half without touching LDS.
+__device__ __forceinline__ float xhalf_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ u32x4 zero_u32x4() {
     u32x4 z;

@@ -44,7 +44,36 @@ __device__ __forceinline__ void map_workgroup(int w, int total, int n_qtiles, in
 // ---------------------------------------------------------------------------
 // bf16 inputs, bf16 output, fp32 accumulation.  BR = 128 (4 waves x 32 rows),
 // BC = 64 keys per tile.
+//
+// K and V tiles go from HBM straight into LDS (buffer_load ... lds: no VGPR
+// staging), row-major with 16-byte chunks permuted by kv_swizzle.  Operands:
+//   K  (A of S^T = K Q^T)   : ds_read_b128, 8 consecutive d of one key row.
+//   V^T(A of O^T += V^T P^T): two ds_read_b64_tr_b16 per MFMA.  Within each
+//       16-lane group that read hands lane i element e of the 8 bytes read by
+//       lane 4e + i/4 (element i%4), so if those lanes read 4 key rows x 16
+//       dv columns, lane i receives 4 consecutive keys of dv column i -- the
+//       key-contiguous V^T operand, with V itself stored untransposed.
 // ---------------------------------------------------------------------------
+
+// 16-byte-chunk permutation of a row-major [rows][D] bf16 tile in LDS.  It
+// is chosen so that (a) 16 consecutive rows read at one logical chunk (the K
+// operand reads) and (b) 4 consecutive rows x 4 consecutive chunks (one
+// 32-lane half of a V transpose read) each land on distinct bank groups.
+template <int D>
+__device__ __forceinline__ uint32_t kv_swizzle(uint32_t row) {
+    if constexpr (D == 128) {
+        return ((row & 3u) << 2) | ((row >> 2) & 3u);
+    } else {
+        const uint32_t j = row >> 1;
+        return ((j & 1u) << 2) | ((j >> 1) & 3u);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t kv_offset(uint32_t row, uint32_t chunk) {
+    return row * (D * 2) + ((chunk ^ kv_swizzle<D>(row)) << 4);
+}
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     constexpr int BR = 128, BC = 64;
@@ -52,14 +81,13 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     constexpr int NKB = BC / 32;       // 32-key blocks per tile
     constexpr int NDB = D / 32;        // 32-row blocks of O^T
     constexpr int NKC = BC / 16;       // 16-key k-steps for O^T += V^T P^T
-    constexpr int K_BYTES = BC * D * 2;
-    constexpr int BUF_BYTES = 2 * K_BYTES;          // K tile + V^T tile
-    constexpr int KCH = BC * D / 8 / 256;           // 16 B chunks of K per thread
-    constexpr int VUN = (BC / 4) * (D / 8);         // 4-key x 8-dv units of V
-    constexpr int VPT = (VUN + 255) / 256;
-    static_assert(KCH >= 1 && BC * D / 8 % 256 == 0, "K tile must split evenly");
+    constexpr int T_BYTES = BC * D * 2;              // one K or V tile
+    constexpr int BUF_BYTES = 2 * T_BYTES;           // K tile + V tile
+    constexpr int ROWS_PER_LOAD = 1024 / (D * 2);    // rows one 64-lane x 16 B load covers
+    constexpr int LOADS_PER_WAVE = T_BYTES / 1024 / 4;
+    static_assert(T_BYTES % 4096 == 0, "tile splits into 4 waves x 1 KiB loads");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hg = lane >> 5;
@@ -79,13 +107,37 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
     const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;   // same, per wave
 
+    // Buffer resources over this head's Q, K and V: rows past Nq / Nk read as
+    // zero, so ragged tails need no branches.
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, (uint32_t)Nq * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (uint32_t)Nk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, (uint32_t)Nk * D * 2);
+
+    // Per-lane global byte offsets of the tile chunks this lane moves (loop
+    // invariant; the tile start goes in the scalar offset).  Load i of this
+    // wave fills LDS bytes [(wave*LPW + i) * 1024, +1024) linearly, lane by
+    // lane, so the lane fetches the logical chunk that the swizzle puts there.
+    uint32_t goff[LOADS_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+        const uint32_t lin = (uint32_t)((wave * LOADS_PER_WAVE + i) * 1024 + lane * 16);
+        const uint32_t row = lin / (D * 2), pch = (lin % (D * 2)) / 16;
+        goff[i] = row * (D * 2) + ((pch ^ kv_swizzle<D>(row)) << 4);
+    }
+    auto load_tile = [&](int k0, char* buf) {
+        const uint32_t soff = (uint32_t)k0 * D * 2;
+#pragma unroll
+        for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+            char* dst = buf + (wave * LOADS_PER_WAVE + i) * 1024;
+            buf_load_lds16(rk, dst, goff[i], soff);
+            buf_load_lds16(rv, dst + T_BYTES, goff[i], soff);
+        }
+    };
+
     bf16x8 qreg[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 t = zero_u32x4();
-        if (qi < Nq) t = ldg128(Qh + (size_t)qi * D + 16 * kk + 8 * hg);
-        qreg[kk] = __builtin_bit_cast(bf16x8, t);
-    }
+    for (int kk = 0; kk < NKK; ++kk)
+        qreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rq, (uint32_t)qi * D * 2 + (16 * kk + 8 * hg) * 2, 0));
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -93,64 +145,26 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     float m_run = -INFINITY;   // running max of scale*log2e*S for this lane's query
     float l_run = 0.f;         // partial running sum over this lane's keys
 
-    u32x4 kst[KCH];
-    u32x4 vst[VPT][4];
-
-    auto load_tile = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + 256 * i, r = c / (D / 8), cc = c % (D / 8);
-            kst[i] = (k0 + r < Nk) ? ldg128(Kh + (size_t)(k0 + r) * D + cc * 8) : zero_u32x4();
-        }
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int unit = tid + 256 * u;
-            if (unit < VUN) {
-                const int kg = unit / (D / 8), dc = unit % (D / 8);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int key = k0 + 4 * kg + j;
-                    vst[u][j] = key < Nk ? ldg128(Vh + (size_t)key * D + dc * 8) : zero_u32x4();
-                }
-            }
-        }
-    };
-    auto store_tile = [&](char* buf) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + 256 * i, r = c / (D / 8), cc = c % (D / 8);
-            *(u32x4*)(buf + swz<D * 2>(r, cc)) = kst[i];
-        }
-        char* vt = buf + K_BYTES;
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int unit = tid + 256 * u;
-            if (unit < VUN) {
-                const int kg = unit / (D / 8), dc = unit % (D / 8);
-                u32x2 cols[8];
-                transpose4x8(vst[u], cols);
-                const uint32_t pos = (kg >> 2) * 16 + kperm((kg & 3) * 4);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t row = dc * 8 + e;
-                    *(u32x2*)(vt + swz<BC * 2>(row, pos >> 3) + (pos & 4u) * 2) = cols[e];
-                }
-            }
-        }
-    };
+    // LDS byte offsets (within a tile) of this lane's operand reads.
+    //   K : row kb*32 + l32, logical chunk 2kk + hg.
+    //   V : transpose read r of k-step kc for dv block db: the lane supplies
+    //       row kc*16 + 8r + 4hg + (i>>2) and columns db*32 + (l32 & 16) + 4(i&3).
+    const int gi = lane & 15;
+    uint32_t vrow_base = 4 * hg + (gi >> 2);
+    uint32_t vcol = (uint32_t)((l32 & 16) + 4 * (gi & 3));
 
     if (ntiles > 0) {
-        load_tile(0);
-        store_tile(smem);
+        load_tile(0, smem);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile and Q are in
+        __syncthreads();
     }
-    __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * BC;
         const char* kbuf = smem + (t & 1) * BUF_BYTES;
-        const char* vtbuf = kbuf + K_BYTES;
+        const char* vbuf = kbuf + T_BYTES;
         const bool has_next = t + 1 < ntiles;
-        if (has_next) load_tile(k0 + BC);
+        if (has_next) load_tile(k0 + BC, smem + ((t + 1) & 1) * BUF_BYTES);
 
         if (k0 < kend_w) {
             // ---- S^T = K Q^T (fp32 accumulators) ----
@@ -161,7 +175,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
             for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    const bf16x8 a = *(const bf16x8*)(kbuf + swz<D * 2>(kb * 32 + l32, 2 * kk + hg));
+                    const bf16x8 a = *(const bf16x8*)(kbuf + kv_offset<D>(kb * 32 + l32, 2 * kk + hg));
                     s[kb] = mfma_bf16(a, qreg[kk], s[kb]);
                 }
             }
@@ -183,7 +197,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = xhalf_max(mx);
             const float m_new = fmaxf(m_run, mx * p.scale_log2);
             // a row with no visible key so far keeps base 0: every term is 0
             const float base = (m_new == -INFINITY) ? 0.f : m_new;
@@ -200,9 +214,6 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
                     pw[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
                 }
             }
-            bf16x8 pb[NKC];
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) pb[kc] = __builtin_bit_cast(bf16x8, pw[kc]);
             l_run = alpha * l_run + rs;
             m_run = m_new;
 #pragma unroll
@@ -212,20 +223,26 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
             // ---- O^T += V^T P^T ----
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kc]);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 a = *(const bf16x8*)(vtbuf + swz<BC * 2>(db * 32 + l32, 2 * kc + hg));
-                    oacc[db] = mfma_bf16(a, pb[kc], oacc[db]);
+                    const uint32_t row0 = kc * 16 + vrow_base;
+                    const uint32_t col = db * 32 + vcol;
+                    const bf16x4 lo = lds_read_tr16(vbuf + kv_offset<D>(row0, col >> 3) + (col & 4) * 2);
+                    const bf16x4 hi = lds_read_tr16(vbuf + kv_offset<D>(row0 + 8, col >> 3) + (col & 4) * 2);
+                    oacc[db] = mfma_bf16(concat8(lo, hi), pb, oacc[db]);
                 }
             }
         }
 
-        if (has_next) store_tile(smem + ((t + 1) & 1) * BUF_BYTES);
+        if (has_next) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next tile landed
+        }
         __syncthreads();
     }
 
     // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l) ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = xhalf_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qi < Nq) {
         bf16* Oh = (bf16*)p.o + (size_t)bh * Nq * D + (size_t)qi * D;
@@ -242,7 +259,6 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
             p.lse[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
-
 // ---------------------------------------------------------------------------
 // fp32 inputs and output: true fp32 products on the 32x32x2 fp32 MFMA.
 // BR = BC = 64 (2 waves x 32 rows); single-buffered LDS.

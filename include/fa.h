@@ -72,8 +72,8 @@ typedef enum {
     FA_ERR_SCALE = -8       /* scale is not finite or not > 0                */
 } fa_status_t;
 
-/* Largest Nq or Nk accepted (keeps every in-head index within 32 bits). */
-#define FA_MAX_SEQ (1 << 24)
+/* Largest Nq or Nk accepted (keeps every in-head byte offset within 32 bits). */
+#define FA_MAX_SEQ (1 << 23)
 
 /*
  * Forward pass ("01 · IO-awareness、online softmax 与 tiling" §3;

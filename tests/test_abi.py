@@ -57,7 +57,7 @@ def fwd(**kw):
 def test_fwd_validation_codes():
     assert fwd(B=-1) == -2
     assert fwd(Nq=-3) == -2
-    assert fwd(Nk=(1 << 24) + 1) == -2
+    assert fwd(Nk=(1 << 23) + 1) == -2
     assert fwd(d=96) == -3
     assert fwd(d=256) == -3
     assert fwd(dtype=7) == -4
