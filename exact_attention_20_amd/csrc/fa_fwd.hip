@@ -74,6 +74,10 @@ __device__ __forceinline__ uint32_t kv_offset(uint32_t row, uint32_t chunk) {
     return row * (D * 2) + ((chunk ^ kv_swizzle<D>(row)) << 4);
 }
 
+// Slack (log2 units) the scaling base may lag the true row maximum before O
+// and l are rescaled: P values stay <= 2^8, far inside bf16 and fp32 range.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     constexpr int BR = 128, BC = 64;
@@ -192,34 +196,48 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
                     }
             }
             // ---- online softmax update (base-2, scale folded) ----
+            // m_run is the scaling base.  It moves (and O, l are rescaled by
+            // alpha) only when some row's new maximum exceeds it by more than
+            // kRescaleSlack; otherwise P = 2^(s - m_run) <= 2^kRescaleSlack and
+            // nothing is rescaled.  Exact after the final O / l ("FlashAttention
+            // 1～4 全解汇总", FlashAttention-4 conditional softmax rescaling).
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-            mx = xhalf_max(mx);
-            const float m_new = fmaxf(m_run, mx * p.scale_log2);
+            mx = xhalf_max(mx) * p.scale_log2;
+            // The decision is per row (a row that keeps its base multiplies by
+            // exactly 1), so every row's result depends on that row alone; the
+            // branch only skips the work when no row of the wave needs it.
+            const bool grow = mx > m_run + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float m_new = grow ? mx : m_run;
+                // alpha = 0 on a row's first visible tile (m_run = -inf)
+                const float alpha = grow ? exp2_hw(m_run - m_new) : 1.f;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+                m_run = m_new;
+            }
             // a row with no visible key so far keeps base 0: every term is 0
-            const float base = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2_hw(m_run - base);
-            float rs = 0.f;
+            const float base = (m_run == -INFINITY) ? 0.f : m_run;
             u32x4 pw[NKC];
+            float rs0 = 0.f, rs1 = 0.f;   // fp32 row sums (LSE needs fp32 P, not bf16)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) {
                     const float p0 = exp2_hw(fmaf(s[kb][i], p.scale_log2, -base));
                     const float p1 = exp2_hw(fmaf(s[kb][i + 1], p.scale_log2, -base));
-                    rs += p0 + p1;
+                    rs0 += p0;
+                    rs1 += p1;
                     pw[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
                 }
             }
-            l_run = alpha * l_run + rs;
-            m_run = m_new;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            l_run += rs0 + rs1;
             // ---- O^T += V^T P^T ----
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
