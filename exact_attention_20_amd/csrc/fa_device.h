@@ -113,6 +113,43 @@ __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* l
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, soff, 0, 0);
 }
 
+// The same 16-byte HBM -> LDS copy issued through inline asm, so the
+// compiler's memory-wait analysis does not see it: it would otherwise wait
+// for the copy before every LDS read and every barrier, since it cannot tell
+// which LDS buffer the copy fills.  Completion MUST be awaited explicitly
+// with vmem_wait_all() before any wave reads the destination.
+//   rsrc: raw buffer descriptor words (wave-uniform);
+//   lds_addr: LDS byte address of lane 0's 16 bytes (wave-uniform).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);   // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+__device__ __forceinline__ void async_load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+    // M0 holds the LDS destination; one wait state between the M0 write and
+    // the load that reads it.
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ void vmem_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ds_read_b64_tr_b16 (gfx950): inside each 16-lane group, lane i receives
 // element i%4 of the 8 bytes read by lanes 4e + i/4, e = 0..3.
 __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {

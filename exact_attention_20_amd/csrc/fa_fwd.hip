@@ -183,6 +183,16 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
                     s[kb] = mfma_bf16(a, qreg[kk], s[kb]);
                 }
             }
+            // Keep 8 K-operand reads in flight ahead of the MFMAs (LDS latency
+            // is several MFMAs long): 8 reads, then alternate MFMA / read.
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < NKK * NKB - 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             // ---- mask: only tiles that straddle the diagonal or the tail ----
             const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw + off);
             if (need_mask) {
