@@ -100,6 +100,112 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
                       f"{t_total:.1f} s; numpy exp single-threaded, BLAS {threads} threads"}
 
 
+def time_launches(fn, stream, steps: int, warmup: int) -> float:
+    """Average ms per call of ``fn`` with HIP events on ``stream``."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def train_step_timing(fa, wl, steps: int, warmup: int):
+    """fa_fwd then fa_bwd on the training-step workload (B=4 H=16 N=4096
+    d=64 bf16 causal), each timed on its own with HIP events; inputs, outputs
+    and the backward workspace are resident before timing starts."""
+    import torch
+    w = wl.TRAIN_STEP
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in wl.workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    fwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), fa.FA_BF16, sh)
+    bwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), fa.FA_BF16,
+                ws.data_ptr(), need, sh)
+
+    def fwd():
+        st = fa.fa_fwd(*fwd_args)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd")
+
+    def bwd():
+        st = fa.fa_bwd(*bwd_args)
+        if st != 0:
+            raise fa.FAError(st, "fa_bwd")
+
+    fwd()
+    ms_f = time_launches(fwd, stream, steps, warmup)
+    ms_b = time_launches(bwd, stream, steps, warmup)
+    pairs = visible_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
+    return {"workload": w.name, "shape": w.describe(),
+            "fwd_ms": round(ms_f, 5), "fwd_tflops": round(4 * w.d * pairs / ms_f / 1e9, 3),
+            "bwd_ms": round(ms_b, 5), "bwd_tflops": round(10 * w.d * pairs / ms_b / 1e9, 3),
+            "bwd_flops": 10 * w.d * pairs,
+            "note": "bwd = D pre-pass + main kernel + dq convert; 10*d FLOPs per visible pair"}
+
+
+def _counter_means(csv_dir: str, counter: str):
+    """Per-kernel mean of one rocprofv3 --pmc counter (KiB per dispatch for
+    FETCH_SIZE / WRITE_SIZE) from the counter_collection CSVs in csv_dir."""
+    import csv
+    import glob
+    sums = {}
+    for path in glob.glob(os.path.join(csv_dir, "*counter_collection.csv")):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                acc = sums.setdefault(row["Kernel_Name"], [0.0, 0])
+                acc[0] += float(row["Counter_Value"])
+                acc[1] += 1
+    return {k: v[0] / v[1] for k, v in sums.items()}
+
+
+def summarize_counters(workload: str, kernel: str, fetch_dir: str, write_dir: str,
+                       copy_fetch_dir: str, copy_write_dir: str, copy_mib: int) -> dict:
+    """HBM bytes per launch of ``kernel`` from two --pmc runs (FETCH_SIZE,
+    WRITE_SIZE), each scaled by what the same counter reads for a plain
+    device copy of ``copy_mib`` MiB; written to profiles/traffic.json."""
+    copy_bytes = copy_mib << 20
+    cf = max(v for k, v in _counter_means(copy_fetch_dir, "FETCH_SIZE").items() if "copy" in k.lower())
+    cw = max(v for k, v in _counter_means(copy_write_dir, "WRITE_SIZE").items() if "copy" in k.lower())
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    fk = _counter_means(fetch_dir, "FETCH_SIZE")[kernel] * 1024.0 * f_scale
+    wk = _counter_means(write_dir, "WRITE_SIZE")[kernel] * 1024.0 * w_scale
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        t = {"kernel_source_hash": kernel_source_hash(), "workloads": {}}
+    t["workloads"][workload] = {
+        "kernel": kernel, "hbm_bytes_per_launch": int(fk + wk),
+        "fetch_bytes": int(fk), "write_bytes": int(wk),
+        "copy_calibration": {"bytes": copy_bytes, "fetch_scale": round(f_scale, 4),
+                             "write_scale": round(w_scale, 4)},
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    return t["workloads"][workload]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,10 +213,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama_causal_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train-step", action="store_true",
+                    help="skip the forward+backward timing on the training-step workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(reference kernel for scaling the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=5,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "COPY_MIB"),
+                    help="write profiles/traffic.json for --workload from rocprofv3 --pmc output "
+                         "directories (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        fd, wd, cfd, cwd, mib = args.summarize_counters
+        kern = "fwd_bf16_kernel" if "bf16" in args.workload else "fwd_f32_kernel"
+        print(json.dumps(summarize_counters(args.workload, kern, fd, wd, cfd, cwd, int(mib))))
+        return
     if args.copy_calibration:
         import torch
         n = args.copy_calibration << 20
@@ -185,6 +302,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
     }
+    if not args.no_train_step:
+        result["train_step"] = train_step_timing(fa, wl, steps=20, warmup=5)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(result), flush=True)

@@ -114,8 +114,6 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     // Buffer resources over this head's Q, K and V: rows past Nq / Nk read as
     // zero, so ragged tails need no branches.
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, (uint32_t)Nq * D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (uint32_t)Nk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, (uint32_t)Nk * D * 2);
 
     // Per-lane global byte offsets of the tile chunks this lane moves (loop
     // invariant; the tile start goes in the scalar offset).  Load i of this
@@ -128,13 +126,20 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
         const uint32_t row = lin / (D * 2), pch = (lin % (D * 2)) / 16;
         goff[i] = row * (D * 2) + ((pch ^ kv_swizzle<D>(row)) << 4);
     }
+    // The copies go through async_load_lds16 (invisible to the compiler's
+    // wait analysis): with the builtin form the compiler waits for the copy
+    // of tile t+1 before the first V read of tile t, which puts a full HBM /
+    // L2 round trip inside every tile.  Completion is awaited explicitly at
+    // the end-of-tile barrier instead.
+    const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
+    const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
     auto load_tile = [&](int k0, char* buf) {
         const uint32_t soff = (uint32_t)k0 * D * 2;
 #pragma unroll
         for (int i = 0; i < LOADS_PER_WAVE; ++i) {
             char* dst = buf + (wave * LOADS_PER_WAVE + i) * 1024;
-            buf_load_lds16(rk, dst, goff[i], soff);
-            buf_load_lds16(rv, dst + T_BYTES, goff[i], soff);
+            async_load_lds16(rk_w, lds_address(dst), goff[i], soff);
+            async_load_lds16(rv_w, lds_address(dst + T_BYTES), goff[i], soff);
         }
     };
 
@@ -159,7 +164,10 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
 
     if (ntiles > 0) {
         load_tile(0, smem);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile and Q are in
+        // vmcnt(0) through the builtin so the compiler also knows Q is resident
+        // (and adds no Q waits inside the loop, where they would stall on the
+        // in-flight copies); the hardware counter covers the tile copies too.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     }
 
@@ -263,9 +271,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
             }
         }
 
-        if (has_next) {
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next tile landed
-        }
+        if (has_next) vmem_wait_all();   // this wave's copies of the next tile landed
         __syncthreads();
     }
 
