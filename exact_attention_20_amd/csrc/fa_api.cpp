@@ -62,11 +62,8 @@ extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, in
     if (check_common(B, H, Nq, Nk, d, 1.0f, dtype) != FA_OK) return 0;
     if (dtype != FA_BF16) return 0;
     const size_t rows = (size_t)B * H * Nq;
-    size_t acc = rows * d * sizeof(float);
-    acc = (acc + 255) & ~(size_t)255;
-    size_t vec = rows * sizeof(float);
-    vec = (vec + 255) & ~(size_t)255;
-    return acc + vec;
+    const size_t vec = (rows * sizeof(float) + 255) & ~(size_t)255;
+    return 2 * vec;
 }
 
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -88,7 +85,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
     if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
 
     const size_t rows = (size_t)BH * Nq;
-    size_t acc_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+    const size_t vec_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
     fa::BwdParams p;
     p.q = q;
     p.k = k;
@@ -99,8 +96,8 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
-    p.dq_acc = (float*)workspace;
-    p.dvec = (float*)((char*)workspace + acc_bytes);
+    p.lse2 = (float*)workspace;
+    p.dvec = (float*)((char*)workspace + vec_bytes);
     p.Nq = Nq;
     p.Nk = Nk;
     p.BH = (int)BH;

@@ -5,33 +5,40 @@
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three launches on the caller's stream:
-//   1. prep   : D = rowsum(dO * O) in fp32, and zero the fp32 dQ accumulator.
-//   2. main   : one workgroup per (batch*head, 128-key tile), the loop order of
-//               §5 (fix a key tile, walk the query tiles that can see it).
-//               dK and dV stay in registers for the whole walk; each query
-//               tile's dQ contribution is added into the fp32 accumulator
-//               with float atomics.
-//   3. convert: dq = dQ accumulator * scale, rounded to the output dtype.
+// Three launches on the caller's stream, no atomics (deterministic):
+//   1. prep : per query row, D = rowsum(dO * O) and LSE in log2 units
+//             (+inf for a row with no visible key, so its P is exactly 0).
+//   2. dK/dV: one workgroup per (batch*head, 128-key tile) walking the query
+//             tiles that can see it (the loop order of §5).  Each wave owns 32
+//             keys: K and V sit in registers, Q / dO tiles stream through LDS,
+//             dK and dV accumulate in registers for the whole walk.
+//   3. dQ   : one workgroup per (batch*head, 128-query tile) walking the key
+//             tiles it can see, like the forward pass.  Each wave owns 32
+//             queries: Q and dO sit in registers, K / V tiles stream through
+//             LDS, dQ accumulates in registers.
+// S and dP are computed in both 2 and 3 (7 products instead of 5) in exchange
+// for no dQ atomics and no dS round trip through memory.
 //
-// Register formulation (32x32x16 bf16 MFMA, fp32 accumulate), per wave of 32
-// keys: S = Q K^T and dP = dO V^T come out with lane = key and 16 queries
-// per lane, which is exactly the B-operand shape of the two products that
-// contract over queries (dV^T = dO^T P, dK^T = Q^T dS); the A operands are
-// q-permuted transposed copies of the Q and dO tiles in LDS.  dQ contracts
-// over keys, so dS goes through LDS once per query tile.
+// Register formulation (32x32x16 bf16 MFMA, fp32 accumulate).  In each main
+// kernel the products over the head dimension (S, dP) take the streamed tile
+// as the A operand (ds_read_b128 rows) and the resident operand from
+// registers, so each lane ends up owning ONE row of the resident side (a key
+// in 2, a query in 3) with 16 of its partners per 32-block -- exactly the B
+// operand layout of the products over the streamed side (dV^T += dO^T P and
+// dK^T += Q^T dS in 2, dQ^T += K^T dS^T in 3), whose A operands are
+// transposed reads (ds_read_b64_tr_b16) of the same LDS tiles.
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// 1. D_i = sum_d dO_i * O_i; zero the dQ accumulator row.
+// 1. D_i = sum_d dO_i * O_i (fp32); LSE_i * log2(e), or +inf for an empty row.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
-                                                       float* __restrict__ dvec, float* __restrict__ dq_acc,
-                                                       long rows) {
+                                                       const float* __restrict__ lse, float* __restrict__ dvec,
+                                                       float* __restrict__ lse2, long rows) {
     constexpr int TPR = D / 8;      // threads per row, 8 bf16 each
     constexpr int RPB = 256 / TPR;  // rows per block
     const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -42,217 +49,200 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const bf16* __restrict__ 
         const u32x4 b = ldg128(dO + row * D + c * 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(b[i]) + bf16_hi(a[i]) * bf16_hi(b[i]);
-        f32x4 z;
-        z[0] = z[1] = z[2] = z[3] = 0.f;
-        *(f32x4*)(dq_acc + row * D + c * 8) = z;
-        *(f32x4*)(dq_acc + row * D + c * 8 + 4) = z;
     }
 #pragma unroll
     for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (row < rows && c == 0) dvec[row] = acc;
+    if (row < rows && c == 0) {
+        dvec[row] = acc;
+        const float L = lse[row];
+        lse2[row] = L == -INFINITY ? INFINITY : L * kLog2e;
+    }
+}
+
+// Pack the P (or dS) values of a 32x32 accumulator into the bf16 B operands
+// of two 16-wide k-steps: item i = 4g + e of the accumulator (partner
+// 8g + 4*(lane/32) + e of the block) goes to k-step (g/2), slot 4(g%2) + e,
+// which is the order tile_read_tr hands out the matching rows.
+__device__ __forceinline__ void pack_pairs(const float (&x)[16], u32x4& lo, u32x4& hi) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        lo[i >> 1] = pack_bf16x2(x[i], x[i + 1]);
+        hi[i >> 1] = pack_bf16x2(x[8 + i], x[8 + i + 1]);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// 2. main backward kernel
+// 2. dK, dV.  BKV = 128 keys per workgroup (4 waves x 32), BQ = 64 queries per
+// step.  LDS per stage: Q tile, dO tile (swizzled [BQ][D] bf16) and the BQ
+// values of LSE*log2e and D; two stages, the next one filled while the
+// current one is used.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
-    constexpr int BKV = 128;                 // keys per workgroup: 4 waves x 32
-    constexpr int BQ = D == 64 ? 64 : 32;    // queries per step
-    constexpr int NQB = BQ / 32;             // 32-query blocks per step
-    constexpr int NQC = BQ / 16;             // 16-query k-steps (products over q)
-    constexpr int NKK = D / 16;              // 16-wide k-steps over d
-    constexpr int NDB = D / 32;              // 32-row blocks over d
-    constexpr int QROW = D * 2;              // bytes of a row-major [*, D] tile row
-    constexpr int TROW = BQ * 2;             // bytes of a transposed [D, BQ] tile row
-    constexpr int SROW = BKV * 2;            // bytes of a dS / K^T row
-    constexpr int UN = (BQ / 4) * (D / 8);   // 4-row x 8-col units per staged tile
-    static_assert(NQB * NDB == 4, "one 32x32 dQ block per wave");
-    static_assert(2 * UN <= 256, "one staging unit per thread");
+__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParams p) {
+    constexpr int BKV = 128, BQ = 64;
+    constexpr int NQB = BQ / 32;              // 32-query blocks per step
+    constexpr int NQC = BQ / 16;              // 16-query k-steps
+    constexpr int NKK = D / 16;               // 16-wide k-steps over d
+    constexpr int NDB = D / 32;               // 32-row blocks of dK^T / dV^T
+    constexpr int T_BYTES = BQ * D * 2;       // one Q or dO tile
+    constexpr int V_OFF = 2 * T_BYTES;        // row vectors after the two tiles
+    constexpr int STAGE = V_OFF + 2 * BQ * 4; // + LSE2[BQ] + D[BQ]
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-    __shared__ __attribute__((aligned(16))) char qs[BQ * QROW];
-    __shared__ __attribute__((aligned(16))) char dos[BQ * QROW];
-    __shared__ __attribute__((aligned(16))) char qts[D * TROW];
-    __shared__ __attribute__((aligned(16))) char dots[D * TROW];
-    __shared__ __attribute__((aligned(16))) char dss[BQ * SROW];
-    __shared__ __attribute__((aligned(16))) char kts[D * SROW];
-    __shared__ __attribute__((aligned(16))) float lse2s[BQ];
-    __shared__ __attribute__((aligned(16))) float dvs[BQ];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hg = lane >> 5;
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
     const int n_kt = (Nk + BKV - 1) / BKV;
-    const int bh = blockIdx.x / n_kt;
-    const int kt = blockIdx.x - bh * n_kt;
+    int bh, kt;
+    map_head_tile(blockIdx.x, p.BH * n_kt, n_kt, bh, kt);   // ascending: heavy causal tiles first
     const int k0 = kt * BKV;
-    const int kj = k0 + wave * 32 + l32;     // this lane's key
+    const int kw = k0 + wave * 32;            // this wave's first key
+    const int kj = kw + l32;                  // this lane's key
 
     const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
     const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
     const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
     const bf16* dOh = (const bf16*)p.dO + (size_t)bh * Nq * D;
-    const float* LSEh = p.lse + (size_t)bh * Nq;
-    const float* Dh = p.dvec + (size_t)bh * Nq;
-    float* dQh = p.dq_acc + (size_t)bh * Nq * D;
 
-    // K^T and V^T as B operands (lane = key, 8 d-values per k-step)
+    // K^T and V^T as B operands: lane = key, 8 consecutive d per k-step
+    // (rows past Nk read as zero; their dK / dV are never written).
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (uint32_t)Nk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, (uint32_t)Nk * D * 2);
     bf16x8 kreg[NKK], vreg[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 a = zero_u32x4(), b = zero_u32x4();
-        if (kj < Nk) {
-            a = ldg128(Kh + (size_t)kj * D + 16 * kk + 8 * hg);
-            b = ldg128(Vh + (size_t)kj * D + 16 * kk + 8 * hg);
-        }
-        kreg[kk] = __builtin_bit_cast(bf16x8, a);
-        vreg[kk] = __builtin_bit_cast(bf16x8, b);
-    }
-    // K^T of the whole key tile into LDS, natural key order (B operand of dQ)
-    for (int u = tid; u < (BKV / 4) * (D / 8); u += 256) {
-        const int kg = u / (D / 8), dc = u % (D / 8);
-        u32x4 r[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = k0 + 4 * kg + j;
-            r[j] = key < Nk ? ldg128(Kh + (size_t)key * D + dc * 8) : zero_u32x4();
-        }
-        u32x2 cols[8];
-        transpose4x8(r, cols);
-        const uint32_t pos = 4 * kg;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            *(u32x2*)(kts + swz<SROW>(dc * 8 + e, pos >> 3) + (pos & 4u) * 2) = cols[e];
+        const uint32_t o = (uint32_t)kj * D * 2 + (16 * kk + 8 * hg) * 2;
+        kreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rk, o, 0));
+        vreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rv, o, 0));
     }
 
-    f32x16 dvacc[NDB], dkacc[NDB];
+    // Query range: a query q sees key j iff j <= q + off (causal), so the
+    // walk starts at the first query tile that sees the tile's first key.
+    const int qstart = CAUSAL ? max(0, k0 - off) : 0;
+    const int qt0 = qstart / BQ;
+    const int n_qt = (Nq + BQ - 1) / BQ;
+    const int wq_first = CAUSAL ? kw - off : 0;   // first query that sees this wave's first key
+
+    const TileCopy<D, BQ, 4> copier(wave, lane);
+    const i32x4 rq_w = make_rsrc_words(Qh, (uint32_t)Nq * D * 2);
+    const i32x4 rdo_w = make_rsrc_words(dOh, (uint32_t)Nq * D * 2);
+    const uint32_t smem_lds = lds_address(smem);
+    auto load_step = [&](int qt, int stage) {
+        const uint32_t base = smem_lds + stage * STAGE;
+        copier.issue(rq_w, qt * BQ, base);
+        copier.issue(rdo_w, qt * BQ, base + T_BYTES);
+    };
+    // The step's LSE2 and D values (one query per lane of wave 0) are loaded
+    // one step ahead into registers and written to the stage's LDS slot just
+    // before the end-of-step barrier.  Rows past Nq get LSE2 = +inf (P = 0).
+    static_assert(BQ == 64, "one query per lane of wave 0");
+    const float* L2h = p.lse2 + (size_t)bh * Nq;
+    const float* Dh = p.dvec + (size_t)bh * Nq;
+    float nl2 = INFINITY, ndd = 0.f;
+    auto fetch_vec = [&](int qt) {
+        const int q = qt * BQ + lane;
+        nl2 = q < Nq ? L2h[q] : INFINITY;
+        ndd = q < Nq ? Dh[q] : 0.f;
+    };
+    auto store_vec = [&](int stage) {
+        float* v = (float*)(smem + stage * STAGE + V_OFF);
+        v[lane] = nl2;
+        v[BQ + lane] = ndd;
+    };
+
+    f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-        dvacc[db] = zero16();
         dkacc[db] = zero16();
+        dvacc[db] = zero16();
     }
 
-    const int qstart = CAUSAL ? max(0, k0 - off) : 0;   // first query that sees key k0
-    const int n_qt = (Nq + BQ - 1) / BQ;
-    const int wq = wave / NDB, wd = wave % NDB;          // this wave's dQ block
-
-    for (int qt = qstart / BQ; qt < n_qt; ++qt) {
-        const int q0 = qt * BQ;
-        __syncthreads();   // the previous step's LDS reads are finished
-        // ---- stage Q and dO, row-major and transposed (q-permuted) ----
-        if (tid < 2 * UN) {
-            const int which = tid / UN, u = tid % UN;
-            const bf16* src = which ? dOh : Qh;
-            char* rm = which ? dos : qs;
-            char* tr = which ? dots : qts;
-            const int rg = u / (D / 8), dc = u % (D / 8);
-            u32x4 r[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int q = q0 + 4 * rg + j;
-                r[j] = q < Nq ? ldg128(src + (size_t)q * D + dc * 8) : zero_u32x4();
-                *(u32x4*)(rm + swz<QROW>(4 * rg + j, dc)) = r[j];
-            }
-            u32x2 cols[8];
-            transpose4x8(r, cols);
-            const uint32_t pos = (rg >> 2) * 16 + kperm((rg & 3) * 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *(u32x2*)(tr + swz<TROW>(dc * 8 + e, pos >> 3) + (pos & 4u) * 2) = cols[e];
+    if (qt0 < n_qt) {
+        load_step(qt0, 0);
+        if (wave == 0) {
+            fetch_vec(qt0);
+            store_vec(0);
         }
-        if (tid < BQ) {
-            const int q = q0 + tid;
-            float l2 = INFINITY, dd = 0.f;   // +inf: P = 0 for rows beyond Nq or without keys
-            if (q < Nq) {
-                const float L = LSEh[q];
-                if (L != -INFINITY) l2 = L * kLog2e;
-                dd = Dh[q];
-            }
-            lse2s[tid] = l2;
-            dvs[tid] = dd;
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K, V registers and the first stage
         __syncthreads();
+    }
 
-        // ---- S = Q K^T and dP = dO V^T (lane = key, items = queries) ----
-        f32x16 s[NQB], dp[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-            s[qb] = zero16();
-            dp[qb] = zero16();
+    for (int qt = qt0; qt < n_qt; ++qt) {
+        const int st = (qt - qt0) & 1;
+        const char* qs = smem + st * STAGE;
+        const char* dos = qs + T_BYTES;
+        const float* l2s = (const float*)(qs + V_OFF);
+        const float* dds = l2s + BQ;
+        const int q0 = qt * BQ;
+        const bool has_next = qt + 1 < n_qt;
+        if (has_next) {
+            load_step(qt + 1, st ^ 1);
+            if (wave == 0) fetch_vec(qt + 1);
         }
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
+
+        if (q0 + BQ - 1 >= wq_first) {
+            // ---- S = Q K^T and dP = dO V^T (lane = key, items = queries) ----
+            f32x16 s[NQB], dp[NQB];
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
-                const bf16x8 a = *(const bf16x8*)(qs + swz<QROW>(qb * 32 + l32, 2 * kk + hg));
-                s[qb] = mfma_bf16(a, kreg[kk], s[qb]);
-                const bf16x8 b = *(const bf16x8*)(dos + swz<QROW>(qb * 32 + l32, 2 * kk + hg));
-                dp[qb] = mfma_bf16(b, vreg[kk], dp[qb]);
+                s[qb] = zero16();
+                dp[qb] = zero16();
             }
-
-        // ---- P = exp2(S*scale*log2e - LSE*log2e), dS = P * (dP - D) ----
-        u32x4 pw[NQC], dsw[NQC];
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
+            for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int ql = qb * 32 + g * 8 + 4 * hg;   // local query of item 4g
-                const f32x4 l2 = *(const f32x4*)(lse2s + ql);
-                const f32x4 dd = *(const f32x4*)(dvs + ql);
-                float pv[4], dsv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * g + e;
-                    const int q = q0 + ql + e;
-                    const bool vis = kj < Nk && (!CAUSAL || kj <= q + off);
-                    const float pe = vis ? exp2_hw(fmaf(s[qb][i], p.scale_log2, -l2[e])) : 0.f;
-                    pv[e] = pe;
-                    dsv[e] = pe * (dp[qb][i] - dd[e]);
-                    // write dS (bf16) for the dQ product: row = local query, col = local key
-                    const int kl = wave * 32 + l32;
-                    *(bf16*)(dss + swz<SROW>(ql + e, kl >> 3) + (kl & 7) * 2) = (bf16)dsv[e];
+                for (int qb = 0; qb < NQB; ++qb) {
+                    s[qb] = mfma_bf16(tile_read_row<D>(qs, qb * 32, kk, lane), kreg[kk], s[qb]);
+                    dp[qb] = mfma_bf16(tile_read_row<D>(dos, qb * 32, kk, lane), vreg[kk], dp[qb]);
                 }
-                const int qc = qb * 2 + (g >> 1);
-                pw[qc][(g & 1) * 2 + 0] = pack_bf16x2(pv[0], pv[1]);
-                pw[qc][(g & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
-                dsw[qc][(g & 1) * 2 + 0] = pack_bf16x2(dsv[0], dsv[1]);
-                dsw[qc][(g & 1) * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+            // ---- P = 2^(S*scale*log2e - LSE2), dS = P * (dP - D) ----
+            const bool need_mask = (q0 + BQ > Nq) || (CAUSAL && q0 + off < kw + 31);
+            u32x4 pw[NQC], dsw[NQC];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                float pv[16], dsv[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int ql = qb * 32 + g * 8 + 4 * hg;   // local query of item 4g
+                    const f32x4 l2 = *(const f32x4*)(l2s + ql);
+                    const f32x4 dd = *(const f32x4*)(dds + ql);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float sv = s[qb][4 * g + e];
+                        if (need_mask) {
+                            const int q = q0 + ql + e;
+                            const bool vis = q < Nq && (!CAUSAL || kj <= q + off);
+                            if (!vis) sv = -INFINITY;
+                        }
+                        const float pe = exp2_hw(fmaf(sv, p.scale_log2, -l2[e]));
+                        pv[4 * g + e] = pe;
+                        dsv[4 * g + e] = pe * (dp[qb][4 * g + e] - dd[e]);
+                    }
+                }
+                pack_pairs(pv, pw[2 * qb], pw[2 * qb + 1]);
+                pack_pairs(dsv, dsw[2 * qb], dsw[2 * qb + 1]);
             }
-
-        // ---- dV^T += dO^T P ;  dK^T += Q^T dS ----
+            // ---- dV^T += dO^T P ;  dK^T += Q^T dS ----
 #pragma unroll
-        for (int qc = 0; qc < NQC; ++qc) {
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[qc]);
-            const bf16x8 sb = __builtin_bit_cast(bf16x8, dsw[qc]);
+            for (int qc = 0; qc < NQC; ++qc) {
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[qc]);
+                const bf16x8 sb = __builtin_bit_cast(bf16x8, dsw[qc]);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16x8 a = *(const bf16x8*)(dots + swz<TROW>(db * 32 + l32, 2 * qc + hg));
-                dvacc[db] = mfma_bf16(a, pb, dvacc[db]);
-                const bf16x8 b = *(const bf16x8*)(qts + swz<TROW>(db * 32 + l32, 2 * qc + hg));
-                dkacc[db] = mfma_bf16(b, sb, dkacc[db]);
+                for (int db = 0; db < NDB; ++db) {
+                    dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qc * 16, db * 32, lane), pb, dvacc[db]);
+                    dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qc * 16, db * 32, lane), sb, dkacc[db]);
+                }
             }
         }
-        __syncthreads();   // dS of all four waves is in LDS
 
-        // ---- dQ[q][d] += sum over this tile's keys of dS[q][key] K[key][d] ----
-        {
-            f32x16 acc = zero16();
-#pragma unroll
-            for (int kc = 0; kc < BKV / 16; ++kc) {
-                const bf16x8 a = *(const bf16x8*)(dss + swz<SROW>(wq * 32 + l32, 2 * kc + hg));
-                const bf16x8 b = *(const bf16x8*)(kts + swz<SROW>(wd * 32 + l32, 2 * kc + hg));
-                acc = mfma_bf16(a, b, acc);
-            }
-            const int dcol = wd * 32 + l32;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int q = q0 + wq * 32 + (i >> 2) * 8 + 4 * hg + (i & 3);
-                if (q < Nq) unsafeAtomicAdd(dQh + (size_t)q * D + dcol, acc[i]);
-            }
+        if (has_next) {
+            if (wave == 0) store_vec(st ^ 1);
+            vmem_wait_all();   // this wave's copies of the next stage landed
         }
+        __syncthreads();
     }
 
-    // ---- dK = scale * dK^T acc, dV = dV^T acc (lane = key, items = d) ----
+    // ---- dK = scale * dK^T, dV = dV^T (lane = key, items = d) ----
     if (kj < Nk) {
         bf16* dKr = (bf16*)p.dk + (size_t)bh * Nk * D + (size_t)kj * D;
         bf16* dVr = (bf16*)p.dv + (size_t)bh * Nk * D + (size_t)kj * D;
@@ -273,20 +263,143 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dq = scale * dQ accumulator, rounded to bf16.
+// 3. dQ.  BQ = 128 queries per workgroup (4 waves x 32), BC = 64 keys per
+// step; K and V tiles double-buffered in LDS exactly as in the forward pass.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) bwd_dq_convert_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
-                                                            long n8, float scale) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const f32x4 a = *(const f32x4*)(acc + i * 8);
-    const f32x4 b = *(const f32x4*)(acc + i * 8 + 4);
-    u32x4 w;
-    w[0] = pack_bf16x2(a[0] * scale, a[1] * scale);
-    w[1] = pack_bf16x2(a[2] * scale, a[3] * scale);
-    w[2] = pack_bf16x2(b[0] * scale, b[1] * scale);
-    w[3] = pack_bf16x2(b[2] * scale, b[3] * scale);
-    *(u32x4*)(dq + i * 8) = w;
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
+    constexpr int BQ = 128, BC = 64;
+    constexpr int NKK = D / 16;
+    constexpr int NKB = BC / 32;
+    constexpr int NDB = D / 32;
+    constexpr int NKC = BC / 16;
+    constexpr int T_BYTES = BC * D * 2;
+    constexpr int BUF_BYTES = 2 * T_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hg = lane >> 5;
+    const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+    const int n_qt = (Nq + BQ - 1) / BQ;
+    int bh, qt;
+    map_head_tile(blockIdx.x, p.BH * n_qt, n_qt, bh, qt);
+    qt = n_qt - 1 - qt;                        // heavy causal tiles first
+    const int q0 = qt * BQ;
+    const int qw = q0 + wave * 32;
+    const int qi = qw + l32;
+
+    const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
+    const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
+    const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
+    const bf16* dOh = (const bf16*)p.dO + (size_t)bh * Nq * D;
+
+    const int kend = CAUSAL ? min(Nk, q0 + BQ + off) : Nk;
+    const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
+    const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
+
+    // this lane's query: Q and dO as B operands, its LSE2 and D
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, (uint32_t)Nq * D * 2);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dOh, (uint32_t)Nq * D * 2);
+    bf16x8 qreg[NKK], doreg[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const uint32_t o = (uint32_t)qi * D * 2 + (16 * kk + 8 * hg) * 2;
+        qreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rq, o, 0));
+        doreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rdo, o, 0));
+    }
+    float l2 = INFINITY, dd = 0.f;             // rows past Nq: P = 0
+    if (qi < Nq) {
+        l2 = p.lse2[(size_t)bh * Nq + qi];
+        dd = p.dvec[(size_t)bh * Nq + qi];
+    }
+
+    const TileCopy<D, BC, 4> copier(wave, lane);
+    const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
+    const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
+    const uint32_t smem_lds = lds_address(smem);
+    auto load_tile = [&](int k0, int buf) {
+        copier.issue(rk_w, k0, smem_lds + buf * BUF_BYTES);
+        copier.issue(rv_w, k0, smem_lds + buf * BUF_BYTES + T_BYTES);
+    };
+
+    f32x16 dqacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dqacc[db] = zero16();
+
+    if (ntiles > 0) {
+        load_tile(0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q, dO registers and the first tiles
+        __syncthreads();
+    }
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int k0 = t * BC;
+        const char* kbuf = smem + (t & 1) * BUF_BYTES;
+        const char* vbuf = kbuf + T_BYTES;
+        const bool has_next = t + 1 < ntiles;
+        if (has_next) load_tile(k0 + BC, (t + 1) & 1);
+
+        if (k0 < kend_w) {
+            // ---- S^T = K Q^T, dP^T = V dO^T (lane = query, items = keys) ----
+            f32x16 s[NKB], dp[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                s[kb] = zero16();
+                dp[kb] = zero16();
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    s[kb] = mfma_bf16(tile_read_row<D>(kbuf, kb * 32, kk, lane), qreg[kk], s[kb]);
+                    dp[kb] = mfma_bf16(tile_read_row<D>(vbuf, kb * 32, kk, lane), doreg[kk], dp[kb]);
+                }
+            // ---- dS^T = P * (dP - D), P = 2^(S*scale*log2e - LSE2) ----
+            const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw + off);
+            u32x4 dsw[NKC];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float dsv[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float sv = s[kb][i];
+                    if (need_mask) {
+                        const int key = k0 + kb * 32 + (i >> 2) * 8 + 4 * hg + (i & 3);
+                        const bool vis = key < Nk && (!CAUSAL || key <= qi + off);
+                        if (!vis) sv = -INFINITY;
+                    }
+                    const float pe = exp2_hw(fmaf(sv, p.scale_log2, -l2));
+                    dsv[i] = pe * (dp[kb][i] - dd);
+                }
+                pack_pairs(dsv, dsw[2 * kb], dsw[2 * kb + 1]);
+            }
+            // ---- dQ^T += K^T dS^T ----
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                const bf16x8 sb = __builtin_bit_cast(bf16x8, dsw[kc]);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    dqacc[db] = mfma_bf16(tile_read_tr<D>(kbuf, kc * 16, db * 32, lane), sb, dqacc[db]);
+            }
+        }
+
+        if (has_next) vmem_wait_all();
+        __syncthreads();
+    }
+
+    // ---- dQ = scale * dQ^T (lane = query, items = d) ----
+    if (qi < Nq) {
+        bf16* dQr = (bf16*)p.dq + (size_t)bh * Nq * D + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = pack_bf16x2(dqacc[db][4 * g] * p.scale, dqacc[db][4 * g + 1] * p.scale);
+                w[1] = pack_bf16x2(dqacc[db][4 * g + 2] * p.scale, dqacc[db][4 * g + 3] * p.scale);
+                *(u32x2*)(dQr + db * 32 + g * 8 + 4 * hg) = w;
+            }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -298,31 +411,26 @@ static hipError_t launch_bwd_d(bool causal, const BwdParams& p, hipStream_t s) {
         const long grid = (rows + RPB - 1) / RPB;
         const bf16* o = (const bf16*)p.o;
         const bf16* dO = (const bf16*)p.dO;
+        const float* lse = p.lse;
         float* dvec = p.dvec;
-        float* acc = p.dq_acc;
+        float* lse2 = p.lse2;
         long r = rows;
-        void* args[] = {&o, &dO, &dvec, &acc, &r};
+        void* args[] = {&o, &dO, &lse, &dvec, &lse2, &r};
         hipError_t e = hipLaunchKernel((const void*)bwd_prep_kernel<D>, dim3((unsigned)grid), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
-    const int n_kt = (p.Nk + 127) / 128;
-    const long grid_main = (long)p.BH * n_kt;
-    if (grid_main > 0) {   // with Nq == 0 the walk is empty and dK = dV = 0 are written
-        BwdParams pp = p;
-        void* args[] = {&pp};
-        const void* fn = causal ? (const void*)bwd_main_kernel<D, true> : (const void*)bwd_main_kernel<D, false>;
-        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_main), dim3(256), args, 0, s);
+    BwdParams pp = p;
+    void* args[] = {&pp};
+    const long grid_kv = (long)p.BH * ((p.Nk + 127) / 128);
+    if (grid_kv > 0) {   // with Nq == 0 the walk is empty and dK = dV = 0 are written
+        const void* fn = causal ? (const void*)bwd_dkdv_kernel<D, true> : (const void*)bwd_dkdv_kernel<D, false>;
+        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
-    if (rows > 0) {
-        const long n8 = rows * D / 8;
-        const float* acc = p.dq_acc;
-        bf16* dq = (bf16*)p.dq;
-        long n = n8;
-        float sc = p.scale;
-        void* args[] = {&acc, &dq, &n, &sc};
-        hipError_t e = hipLaunchKernel((const void*)bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)),
-                                       dim3(256), args, 0, s);
+    const long grid_q = (long)p.BH * ((p.Nq + 127) / 128);
+    if (grid_q > 0) {   // with Nk == 0 every row is empty and dQ = 0 is written
+        const void* fn = causal ? (const void*)bwd_dq_kernel<D, true> : (const void*)bwd_dq_kernel<D, false>;
+        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_q), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

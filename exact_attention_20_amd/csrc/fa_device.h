@@ -139,13 +139,14 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 __device__ __forceinline__ void async_load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
     // M0 holds the LDS destination; one wait state between the M0 write and
     // the load that reads it.
+    // M0 is bound as an input operand, so the compiler writes it and knows
+    // the statement reads it.
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        "buffer_load_dwordx4 %0, %1, %2 offen lds"
         :
-        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc), "s"(soff)
-        : "memory", "m0");
+        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory");
 }
 
 __device__ __forceinline__ void vmem_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -185,6 +186,103 @@ __device__ __forceinline__ u32x4 zero_u32x4() {
     u32x4 z;
     z[0] = z[1] = z[2] = z[3] = 0u;
     return z;
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles of D-wide bf16 rows ([rows][D], row-major, 16-byte chunks
+// permuted per row).  The permutation is chosen so that (a) 16 consecutive
+// rows read at one logical chunk (ds_read_b128 of an MFMA A operand: lane =
+// row, 8 consecutive columns) and (b) 4 consecutive rows x 4 consecutive
+// chunks (one 32-lane half of a ds_read_b64_tr_b16 transposed read) each land
+// on distinct bank groups, so both access patterns are conflict-free.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ uint32_t tile_swizzle(uint32_t row) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if constexpr (D == 128) {
+        return ((row & 3u) << 2) | ((row >> 2) & 3u);
+    } else {
+        const uint32_t j = row >> 1;
+        return ((j & 1u) << 2) | ((j >> 1) & 3u);
+    }
+}
+
+// Byte offset of logical 16-byte chunk `chunk` of row `row` in such a tile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_offset(uint32_t row, uint32_t chunk) {
+    return row * (D * 2) + ((chunk ^ tile_swizzle<D>(row)) << 4);
+}
+
+// Transposed operand read from a swizzled tile: for the 16-row k-step
+// starting at row r0 and the 32 columns starting at c0, returns the MFMA
+// A operand whose lane l holds column c0 + l%32 at the 8 rows the 32x32
+// accumulator layout hands out for k-group l/32:
+//   rows r0 + 4g + {0..3} and r0 + 8 + 4g + {0..3},  g = l / 32.
+// (Two ds_read_b64_tr_b16: inside each 16-lane group, lane i receives
+// element i%4 of the 8 bytes read by lanes 4e + i/4, e = 0..3.)
+template <int D>
+__device__ __forceinline__ bf16x8 tile_read_tr(const char* tile, uint32_t r0, uint32_t c0, int lane) {
+    const uint32_t gi = lane & 15, hg = (lane >> 5) & 1;
+    const uint32_t row = r0 + 4 * hg + (gi >> 2);
+    const uint32_t col = c0 + (lane & 16) + 4 * (gi & 3);
+    const bf16x4 lo = lds_read_tr16(tile + tile_offset<D>(row, col >> 3) + (col & 4) * 2);
+    const bf16x4 hi = lds_read_tr16(tile + tile_offset<D>(row + 8, col >> 3) + (col & 4) * 2);
+    return concat8(lo, hi);
+}
+
+// Row read: lane l gets the 8 columns 8*(2*kk + l/32) .. +7 of row r0 + l%32
+// (the MFMA A operand of a product over the tile's columns).
+template <int D>
+__device__ __forceinline__ bf16x8 tile_read_row(const char* tile, uint32_t r0, int kk, int lane) {
+    return *(const bf16x8*)(tile + tile_offset<D>(r0 + (lane & 31), 2 * kk + ((lane >> 5) & 1)));
+}
+
+// Asynchronous copy of ROWS x D bf16 rows of a contiguous [N][D] array into
+// a swizzled LDS tile by WAVES waves (`wave` must be wave-uniform, e.g. from
+// readfirstlane, so the LDS addresses stay scalar): each wave moves LOADS 1 KiB pieces
+// (64 lanes x 16 bytes), lane by lane in LDS order, fetching the logical
+// chunk the swizzle puts there.  Rows past the buffer resource's end read
+// as zero.  Completion must be awaited with vmem_wait_all() and a barrier.
+template <int D, int ROWS, int WAVES>
+struct TileCopy {
+    static constexpr int BYTES = ROWS * D * 2;
+    static constexpr int LOADS = BYTES / 1024 / WAVES;
+    static_assert(BYTES % (1024 * WAVES) == 0, "tile splits into whole 1 KiB pieces per wave");
+    uint32_t goff[LOADS];
+    uint32_t lds_off;
+    __device__ __forceinline__ TileCopy(int wave, int lane) {
+        lds_off = (uint32_t)(wave * LOADS) * 1024u;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const uint32_t lin = (uint32_t)((wave * LOADS + i) * 1024 + lane * 16);
+            const uint32_t row = lin / (D * 2), pch = (lin % (D * 2)) / 16;
+            goff[i] = row * (D * 2) + ((pch ^ tile_swizzle<D>(row)) << 4);
+        }
+    }
+    // Copy rows [row0, row0 + ROWS) of the array behind `rsrc` into the tile
+    // at LDS byte address `dst` (wave-uniform, like `wave`).  The row offset
+    // goes into the scalar offset: on gfx950 the raw-buffer range check
+    // covers per-lane offset + scalar offset, dword by dword (checked on the
+    // device), so rows past the end still read as zero.
+    __device__ __forceinline__ void issue(const i32x4& rsrc, int row0, uint32_t dst) const {
+        const uint32_t soff = (uint32_t)row0 * D * 2;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) async_load_lds16(rsrc, dst + lds_off + i * 1024, goff[i], soff);
+    }
+};
+
+// Workgroup id -> (batch*head, tile index).  Consecutive workgroup ids go to
+// the 8 XCDs round robin, so ids are regrouped to give each XCD a contiguous
+// run of heads (their K/V, or Q/dO, then share that XCD's L2).  Tiles of a
+// head come out in ascending order.
+__device__ __forceinline__ void map_head_tile(int w, int total, int n_tiles, int& bh, int& tile) {
+    int L = w;
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        L = (w & 7) * per + (w >> 3);
+    }
+    bh = L / n_tiles;
+    tile = L - bh * n_tiles;
 }
 
 }  // namespace fa

@@ -26,19 +26,12 @@
 
 namespace fa {
 
-// Workgroup id -> (batch*head, query tile).  MI300-class parts hand
-// consecutive workgroup ids to the 8 XCDs round robin, so ids are regrouped
-// to give each XCD a contiguous run of heads (their K/V then share that
-// XCD's L2).  Within a head the heaviest (last, for causal) query tile is
+// Workgroup id -> (batch*head, query tile): XCD-grouped heads (see
+// map_head_tile); within a head the heaviest (last, for causal) query tile is
 // issued first so the short tiles fill the tail.
 __device__ __forceinline__ void map_workgroup(int w, int total, int n_qtiles, int& bh, int& qt) {
-    int L = w;
-    if ((total & 7) == 0) {
-        const int per = total >> 3;
-        L = (w & 7) * per + (w >> 3);
-    }
-    bh = L / n_qtiles;
-    qt = n_qtiles - 1 - (L - bh * n_qtiles);
+    map_head_tile(w, total, n_qtiles, bh, qt);
+    qt = n_qtiles - 1 - qt;
 }
 
 // ---------------------------------------------------------------------------
@@ -46,7 +39,7 @@ __device__ __forceinline__ void map_workgroup(int w, int total, int n_qtiles, in
 // BC = 64 keys per tile.
 //
 // K and V tiles go from HBM straight into LDS (buffer_load ... lds: no VGPR
-// staging), row-major with 16-byte chunks permuted by kv_swizzle.  Operands:
+// staging), row-major with 16-byte chunks permuted by tile_swizzle.  Operands:
 //   K  (A of S^T = K Q^T)   : ds_read_b128, 8 consecutive d of one key row.
 //   V^T(A of O^T += V^T P^T): two ds_read_b64_tr_b16 per MFMA.  Within each
 //       16-lane group that read hands lane i element e of the 8 bytes read by
@@ -54,25 +47,6 @@ __device__ __forceinline__ void map_workgroup(int w, int total, int n_qtiles, in
 //       dv columns, lane i receives 4 consecutive keys of dv column i -- the
 //       key-contiguous V^T operand, with V itself stored untransposed.
 // ---------------------------------------------------------------------------
-
-// 16-byte-chunk permutation of a row-major [rows][D] bf16 tile in LDS.  It
-// is chosen so that (a) 16 consecutive rows read at one logical chunk (the K
-// operand reads) and (b) 4 consecutive rows x 4 consecutive chunks (one
-// 32-lane half of a V transpose read) each land on distinct bank groups.
-template <int D>
-__device__ __forceinline__ uint32_t kv_swizzle(uint32_t row) {
-    if constexpr (D == 128) {
-        return ((row & 3u) << 2) | ((row >> 2) & 3u);
-    } else {
-        const uint32_t j = row >> 1;
-        return ((j & 1u) << 2) | ((j >> 1) & 3u);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ uint32_t kv_offset(uint32_t row, uint32_t chunk) {
-    return row * (D * 2) + ((chunk ^ kv_swizzle<D>(row)) << 4);
-}
 
 // Slack (log2 units) the scaling base may lag the true row maximum before O
 // and l are rescaled: P values stay <= 2^8, far inside bf16 and fp32 range.
@@ -87,13 +61,12 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     constexpr int NKC = BC / 16;       // 16-key k-steps for O^T += V^T P^T
     constexpr int T_BYTES = BC * D * 2;              // one K or V tile
     constexpr int BUF_BYTES = 2 * T_BYTES;           // K tile + V tile
-    constexpr int ROWS_PER_LOAD = 1024 / (D * 2);    // rows one 64-lane x 16 B load covers
-    constexpr int LOADS_PER_WAVE = T_BYTES / 1024 / 4;
-    static_assert(T_BYTES % 4096 == 0, "tile splits into 4 waves x 1 KiB loads");
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_BYTES];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index through readfirstlane: everything derived from it (LDS
+    // addresses, the per-wave causal limits) stays in scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hg = lane >> 5;
     int bh, qt;
     map_workgroup(blockIdx.x, p.total_wg, p.n_qtiles, bh, qt);
@@ -115,32 +88,18 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     // zero, so ragged tails need no branches.
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, (uint32_t)Nq * D * 2);
 
-    // Per-lane global byte offsets of the tile chunks this lane moves (loop
-    // invariant; the tile start goes in the scalar offset).  Load i of this
-    // wave fills LDS bytes [(wave*LPW + i) * 1024, +1024) linearly, lane by
-    // lane, so the lane fetches the logical chunk that the swizzle puts there.
-    uint32_t goff[LOADS_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-        const uint32_t lin = (uint32_t)((wave * LOADS_PER_WAVE + i) * 1024 + lane * 16);
-        const uint32_t row = lin / (D * 2), pch = (lin % (D * 2)) / 16;
-        goff[i] = row * (D * 2) + ((pch ^ kv_swizzle<D>(row)) << 4);
-    }
     // The copies go through async_load_lds16 (invisible to the compiler's
     // wait analysis): with the builtin form the compiler waits for the copy
     // of tile t+1 before the first V read of tile t, which puts a full HBM /
     // L2 round trip inside every tile.  Completion is awaited explicitly at
     // the end-of-tile barrier instead.
+    const TileCopy<D, BC, 4> copier(wave, lane);
     const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
     const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
-    auto load_tile = [&](int k0, char* buf) {
-        const uint32_t soff = (uint32_t)k0 * D * 2;
-#pragma unroll
-        for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-            char* dst = buf + (wave * LOADS_PER_WAVE + i) * 1024;
-            async_load_lds16(rk_w, lds_address(dst), goff[i], soff);
-            async_load_lds16(rv_w, lds_address(dst + T_BYTES), goff[i], soff);
-        }
+    const uint32_t smem_lds = lds_address(smem);
+    auto load_tile = [&](int k0, int buf) {
+        copier.issue(rk_w, k0, smem_lds + buf * BUF_BYTES);
+        copier.issue(rv_w, k0, smem_lds + buf * BUF_BYTES + T_BYTES);
     };
 
     bf16x8 qreg[NKK];
@@ -154,16 +113,8 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     float m_run = -INFINITY;   // running max of scale*log2e*S for this lane's query
     float l_run = 0.f;         // partial running sum over this lane's keys
 
-    // LDS byte offsets (within a tile) of this lane's operand reads.
-    //   K : row kb*32 + l32, logical chunk 2kk + hg.
-    //   V : transpose read r of k-step kc for dv block db: the lane supplies
-    //       row kc*16 + 8r + 4hg + (i>>2) and columns db*32 + (l32 & 16) + 4(i&3).
-    const int gi = lane & 15;
-    uint32_t vrow_base = 4 * hg + (gi >> 2);
-    uint32_t vcol = (uint32_t)((l32 & 16) + 4 * (gi & 3));
-
     if (ntiles > 0) {
-        load_tile(0, smem);
+        load_tile(0, 0);
         // vmcnt(0) through the builtin so the compiler also knows Q is resident
         // (and adds no Q waits inside the loop, where they would stall on the
         // in-flight copies); the hardware counter covers the tile copies too.
@@ -176,7 +127,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
         const char* kbuf = smem + (t & 1) * BUF_BYTES;
         const char* vbuf = kbuf + T_BYTES;
         const bool has_next = t + 1 < ntiles;
-        if (has_next) load_tile(k0 + BC, smem + ((t + 1) & 1) * BUF_BYTES);
+        if (has_next) load_tile(k0 + BC, (t + 1) & 1);
 
         if (k0 < kend_w) {
             // ---- S^T = K Q^T (fp32 accumulators) ----
@@ -187,20 +138,20 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
             for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    const bf16x8 a = *(const bf16x8*)(kbuf + kv_offset<D>(kb * 32 + l32, 2 * kk + hg));
-                    s[kb] = mfma_bf16(a, qreg[kk], s[kb]);
+                    s[kb] = mfma_bf16(tile_read_row<D>(kbuf, kb * 32, kk, lane), qreg[kk], s[kb]);
                 }
             }
             // Keep 8 K-operand reads in flight ahead of the MFMAs (LDS latency
             // is several MFMAs long): 8 reads, then alternate MFMA / read.
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            constexpr int kAhead = NKK * NKB < 8 ? NKK * NKB : 8;
+            __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-            for (int i = 0; i < NKK * NKB - 8; ++i) {
+            for (int i = 0; i < NKK * NKB - kAhead; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             // ---- mask: only tiles that straddle the diagonal or the tail ----
             const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw + off);
             if (need_mask) {
@@ -261,13 +212,8 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
             for (int kc = 0; kc < NKC; ++kc) {
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kc]);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const uint32_t row0 = kc * 16 + vrow_base;
-                    const uint32_t col = db * 32 + vcol;
-                    const bf16x4 lo = lds_read_tr16(vbuf + kv_offset<D>(row0, col >> 3) + (col & 4) * 2);
-                    const bf16x4 hi = lds_read_tr16(vbuf + kv_offset<D>(row0 + 8, col >> 3) + (col & 4) * 2);
-                    oacc[db] = mfma_bf16(concat8(lo, hi), pb, oacc[db]);
-                }
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] = mfma_bf16(tile_read_tr<D>(vbuf, kc * 16, db * 32, lane), pb, oacc[db]);
             }
         }
 

@@ -30,8 +30,8 @@ struct BwdParams {
     void* dq;
     void* dk;
     void* dv;
-    float* dq_acc;     // [B,H,Nq,d] float32 workspace
-    float* dvec;       // [B,H,Nq]   float32 workspace: rowsum(dO * O)
+    float* lse2;       // [B,H,Nq] float32 workspace: LSE * log2(e), +inf for empty rows
+    float* dvec;       // [B,H,Nq] float32 workspace: rowsum(dO * O)
     int Nq;
     int Nk;
     int BH;

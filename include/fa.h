@@ -90,9 +90,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (float32 dQ
- * accumulator [B,H,Nq,d] plus the float32 row vector D = rowsum(dO * O)
- * [B,H,Nq]), rounded up to 256.  Returns 0 for invalid sizes or dtype.
+ * Bytes of device workspace fa_bwd needs for these sizes: two float32 row
+ * vectors [B,H,Nq] (the LSE in base-2 units and D = rowsum(dO * O)), each
+ * rounded up to 256 bytes.  Returns 0 for invalid sizes or dtype.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
 
@@ -109,9 +109,10 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
  *   workspace: device memory of at least fa_bwd_workspace_bytes(); its
  *   contents on entry are ignored and on exit are unspecified.
  *
- * Only FA_BF16 is accepted (FA_ERR_DTYPE otherwise).  dq is summed over key
- * tiles with float32 atomics, so it is not bitwise reproducible run to run;
- * dk and dv are.  Calls that share a workspace must not overlap.
+ * Only FA_BF16 is accepted (FA_ERR_DTYPE otherwise).  Deterministic: each
+ * of dq, dk and dv is accumulated in registers by one workgroup, so the same
+ * inputs give bitwise the same outputs.  Calls that share a workspace must
+ * not overlap.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dO, void* dq, void* dk, void* dv,

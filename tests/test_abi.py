@@ -83,9 +83,9 @@ def test_fwd_empty_is_a_noop():
 def test_workspace_bytes():
     n = fa.fa_bwd_workspace_bytes(4, 16, 4096, 4096, 64, fa.FA_BF16)
     rows = 4 * 16 * 4096
-    assert n == rows * 64 * 4 + rows * 4       # both parts already 256-aligned
+    assert n == 2 * rows * 4                   # two float32 row vectors, already 256-aligned
     assert n % 256 == 0
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_BF16) == 768 + 256
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_BF16) == 2 * 256
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 96, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_F32) == 0
     assert fa.fa_bwd_workspace_bytes(-1, 1, 3, 5, 64, fa.FA_BF16) == 0
