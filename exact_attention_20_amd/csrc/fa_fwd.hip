@@ -112,6 +112,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < NDB; ++db) oacc[db] = zero16();
     float m_run = -INFINITY;   // running max of scale*log2e*S for this lane's query
     float l_run = 0.f;         // partial running sum over this lane's keys
+    float nbase = 0.f;         // -m_run, or 0 while the row has seen no key (every term is then 0)
 
     if (ntiles > 0) {
         load_tile(0, 0);
@@ -190,24 +191,31 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
                 m_run = m_new;
+                nbase = (m_run == -INFINITY) ? 0.f : -m_run;
             }
-            // a row with no visible key so far keeps base 0: every term is 0
-            const float base = (m_run == -INFINITY) ? 0.f : m_run;
             u32x4 pw[NKC];
-            float rs0 = 0.f, rs1 = 0.f;   // fp32 row sums (LSE needs fp32 P, not bf16)
+            float pv[NKB * 16];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) {
-                    const float p0 = exp2_hw(fmaf(s[kb][i], p.scale_log2, -base));
-                    const float p1 = exp2_hw(fmaf(s[kb][i + 1], p.scale_log2, -base));
-                    rs0 += p0;
-                    rs1 += p1;
+                    const float p0 = exp2_hw(fmaf(s[kb][i], p.scale_log2, nbase));
+                    const float p1 = exp2_hw(fmaf(s[kb][i + 1], p.scale_log2, nbase));
+                    pv[kb * 16 + i] = p0;
+                    pv[kb * 16 + i + 1] = p1;
                     pw[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
                 }
             }
-            l_run += rs0 + rs1;
+            // fp32 row sums (the LSE needs fp32 P, not the bf16 copy), as four
+            // independent chains
+            float rs[4] = {pv[0], pv[1], pv[2], pv[3]};
+#pragma unroll
+            for (int i = 4; i < NKB * 16; ++i) rs[i & 3] += pv[i];
+            l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
             // ---- O^T += V^T P^T ----
+            // raised wave priority while this wave feeds the matrix cores, so
+            // the other wave of the SIMD takes the issue slots the MFMAs leave
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kc]);
@@ -217,6 +225,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
             }
         }
 
+        __builtin_amdgcn_s_setprio(0);
         if (has_next) vmem_wait_all();   // this wave's copies of the next tile landed
         __syncthreads();
     }
