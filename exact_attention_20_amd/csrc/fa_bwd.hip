@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
             store_vec(0);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K, V registers and the first stage
-        __syncthreads();
+        tile_barrier();
     }
 
     for (int qt = qt0; qt < n_qt; ++qt) {
@@ -239,7 +239,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
             if (wave == 0) store_vec(st ^ 1);
             vmem_wait_all();   // this wave's copies of the next stage landed
         }
-        __syncthreads();
+        tile_barrier();
     }
 
     // ---- dK = scale * dK^T, dV = dV^T (lane = key, items = d) ----
@@ -329,7 +329,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     if (ntiles > 0) {
         load_tile(0, 0);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q, dO registers and the first tiles
-        __syncthreads();
+        tile_barrier();
     }
 
     for (int t = 0; t < ntiles; ++t) {
@@ -384,7 +384,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
         }
 
         if (has_next) vmem_wait_all();
-        __syncthreads();
+        tile_barrier();
     }
 
     // ---- dQ = scale * dQ^T (lane = query, items = d) ----

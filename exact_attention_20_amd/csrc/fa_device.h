@@ -137,12 +137,13 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 }
 
 __device__ __forceinline__ void async_load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-    // M0 holds the LDS destination; one wait state between the M0 write and
-    // the load that reads it.
-    // M0 is bound as an input operand, so the compiler writes it and knows
-    // the statement reads it.
+    // M0 holds the LDS destination; it is bound as an input operand, so the
+    // compiler writes it and knows the statement reads it.  The compiler's
+    // hazard checks do not look inside the statement, so it starts with the
+    // wait states the load needs itself: 1 after an SALU write of M0 and 5
+    // after a VALU write (v_readfirstlane / v_readlane) of an SGPR it reads.
     asm volatile(
-        "s_nop 0\n\t"
+        "s_nop 4\n\t"
         "buffer_load_dwordx4 %0, %1, %2 offen lds"
         :
         : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
@@ -150,6 +151,16 @@ __device__ __forceinline__ void async_load_lds16(i32x4 rsrc, uint32_t lds_addr, 
 }
 
 __device__ __forceinline__ void vmem_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier between LDS phases of the tile loops.  The scheduling
+// barriers keep every instruction on its side of it, whatever the machine
+// scheduler's alias reasoning about the asynchronous copies (which it cannot
+// see) would allow.
+__device__ __forceinline__ void tile_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // ds_read_b64_tr_b16 (gfx950): inside each 16-lane group, lane i receives
 // element i%4 of the 8 bytes read by lanes 4e + i/4, e = 0..3.

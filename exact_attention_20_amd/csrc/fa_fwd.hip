@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
         // (and adds no Q waits inside the loop, where they would stall on the
         // in-flight copies); the hardware counter covers the tile copies too.
         __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
+        tile_barrier();
     }
 
     for (int t = 0; t < ntiles; ++t) {
@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
 
         __builtin_amdgcn_s_setprio(0);
         if (has_next) vmem_wait_all();   // this wave's copies of the next tile landed
-        __syncthreads();
+        tile_barrier();
     }
 
     // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l) ----
