@@ -53,7 +53,9 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
     p.Nq = Nq;
     p.Nk = Nk;
     p.n_qtiles = n_qtiles;
-    p.total_wg = (int)(BH * n_qtiles);
+    p.paired = fa::fwd_pair_tiles(dtype, causal != 0, BH, n_qtiles) ? 1 : 0;
+    p.n_slots = p.paired ? (n_qtiles + 1) / 2 : n_qtiles;
+    p.total_wg = (int)(BH * p.n_slots);
     p.scale_log2 = scale * 1.44269504088896340736f;
     return hip_status(fa::launch_fwd(dtype, d, causal != 0, (int)BH, p, (hipStream_t)stream));
 }

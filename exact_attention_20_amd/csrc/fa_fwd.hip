@@ -68,21 +68,17 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     // addresses, the per-wave causal limits) stays in scalar registers
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hg = lane >> 5;
-    int bh, qt;
-    map_workgroup(blockIdx.x, p.total_wg, p.n_qtiles, bh, qt);
+    // The workgroup's query tiles: tile n-1-j, then with pairing its mirror
+    // j of the same head (causal: the two tiles together see n+1 rows of key
+    // tiles whatever j is, so every workgroup gets the same work).
+    int bh, slot;
+    map_head_tile(blockIdx.x, p.total_wg, p.n_slots, bh, slot);
+    const int nqt = p.n_qtiles;
+    const int n_items = (p.paired && slot != nqt - 1 - slot) ? 2 : 1;
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
-    const int q0 = qt * BR;
-    const int qw = q0 + wave * 32;     // this wave's first query
-    const int qi = qw + l32;           // this lane's query
     const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
     const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
     const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
-
-    // Key range this workgroup needs: causal stops after the last key the
-    // tile's last query can see; tiles beyond are skipped entirely.
-    const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
-    const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
-    const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;   // same, per wave
 
     // Buffer resources over this head's Q, K and V: rows past Nq / Nk read as
     // zero, so ragged tails need no branches.
@@ -103,9 +99,29 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     };
 
     bf16x8 qreg[NKK];
+    auto load_q = [&](int qi_) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-        qreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rq, (uint32_t)qi * D * 2 + (16 * kk + 8 * hg) * 2, 0));
+        for (int kk = 0; kk < NKK; ++kk)
+            qreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rq, (uint32_t)qi_ * D * 2 + (16 * kk + 8 * hg) * 2, 0));
+    };
+    // Key tiles a query tile needs: causal stops after the last key its last
+    // query can see; tiles beyond are skipped entirely.
+    auto tiles_of = [&](int qt_) {
+        const int kend_ = CAUSAL ? min(Nk, qt_ * BR + BR + off) : Nk;
+        return kend_ > 0 ? (kend_ + BC - 1) / BC : 0;
+    };
+
+    int b0 = 0;               // LDS buffer of the current item's first key tile
+    bool prefetched = false;  // its Q and first key tile were issued by the previous item
+    for (int it = 0; it < n_items; ++it) {
+    const int qt = it == 0 ? nqt - 1 - slot : slot;
+    const int q0 = qt * BR;
+    const int qw = q0 + wave * 32;     // this wave's first query
+    const int qi = qw + l32;           // this lane's query
+    const int ntiles = tiles_of(qt);
+    const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;   // last key + 1 this wave sees
+    const bool more = it + 1 < n_items;
+    const int next_ntiles = more ? tiles_of(slot) : 0;
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -114,8 +130,9 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     float l_run = 0.f;         // partial running sum over this lane's keys
     float nbase = 0.f;         // -m_run, or 0 while the row has seen no key (every term is then 0)
 
-    if (ntiles > 0) {
-        load_tile(0, 0);
+    if (!prefetched) {
+        load_q(qi);
+        if (ntiles > 0) load_tile(0, b0);
         // vmcnt(0) through the builtin so the compiler also knows Q is resident
         // (and adds no Q waits inside the loop, where they would stall on the
         // in-flight copies); the hardware counter covers the tile copies too.
@@ -125,10 +142,13 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
 
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * BC;
-        const char* kbuf = smem + (t & 1) * BUF_BYTES;
+        const int buf = (b0 + t) & 1;
+        const char* kbuf = smem + buf * BUF_BYTES;
         const char* vbuf = kbuf + T_BYTES;
-        const bool has_next = t + 1 < ntiles;
-        if (has_next) load_tile(k0 + BC, (t + 1) & 1);
+        // the other buffer takes the next key tile, or the next item's first
+        const bool has_next = t + 1 < ntiles || next_ntiles > 0;
+        if (t + 1 < ntiles) load_tile(k0 + BC, buf ^ 1);
+        else if (has_next) load_tile(0, buf ^ 1);
 
         if (k0 < kend_w) {
             // ---- S^T = K Q^T (fp32 accumulators) ----
@@ -230,6 +250,12 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
         tile_barrier();
     }
 
+    // The next item's Q goes into the (now idle) Q registers while this
+    // item's epilogue runs; its first key tile is already in LDS.
+    prefetched = next_ntiles > 0 && ntiles > 0;
+    if (prefetched) load_q(slot * BR + wave * 32 + l32);
+    b0 = (b0 + ntiles) & 1;
+
     // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l) ----
     const float l_tot = xhalf_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -247,6 +273,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
         if (hg == 0 && p.lse)
             p.lse[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
+    }   // items
 }
 // ---------------------------------------------------------------------------
 // fp32 inputs and output: true fp32 products on the 32x32x2 fp32 MFMA.
@@ -382,6 +409,15 @@ __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdParams p) {
 int fwd_rows_per_workgroup(int dtype, int d) {
     (void)d;
     return dtype == 0 ? 64 : 128;
+}
+
+// 256 CUs x 2 resident workgroups = 512 slots; pair when the unpaired grid
+// covers them at least four times and sequences are short enough that a
+// workgroup's start-up (Q and first key tile from HBM) and epilogue are a
+// noticeable share of its work (measured: +10% at N=4096 d=64, none at
+// N=32768 d=128).
+bool fwd_pair_tiles(int dtype, bool causal, long bh, int n_qtiles) {
+    return dtype == 1 && causal && n_qtiles >= 2 && n_qtiles <= 64 && bh * n_qtiles >= 4 * 512;
 }
 
 template <typename KernelT>

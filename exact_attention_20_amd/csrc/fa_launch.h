@@ -16,7 +16,9 @@ struct FwdParams {
     int Nq;
     int Nk;
     int n_qtiles;      // ceil(Nq / BR) for the chosen kernel
-    int total_wg;      // B * H * n_qtiles
+    int n_slots;       // workgroups per (batch, head): n_qtiles, or ceil(n_qtiles / 2) when paired
+    int paired;        // bf16 kernel: a workgroup runs query tiles n-1-j and j of one head
+    int total_wg;      // B * H * n_slots
     float scale_log2;  // scale * log2(e)
 };
 
@@ -41,6 +43,11 @@ struct BwdParams {
 
 // Query rows per forward workgroup for a dtype (used to size the grid).
 int fwd_rows_per_workgroup(int dtype, int d);
+
+// Whether the bf16 forward pairs query tiles (n-1-j with j) in one workgroup:
+// causal only, where it evens out the work, and only for grids large enough
+// that halving the workgroup count still fills the GPU several times over.
+bool fwd_pair_tiles(int dtype, bool causal, long bh, int n_qtiles);
 
 hipError_t launch_fwd(int dtype, int d, bool causal, int BH, FwdParams p, hipStream_t stream);
 hipError_t launch_bwd(int d, bool causal, BwdParams p, hipStream_t stream);

@@ -115,6 +115,36 @@ def test_train_step_forward_sampled_rows():
     _sampled_rows_check(wl.TRAIN_STEP, 96, 5005)
 
 
+# ------------------------------------------ paired query tiles (large causal grids)
+# With causal masking and at least 2048 (batch*head, 128-row query tile) units,
+# a bf16 workgroup runs query tile n-1-j and then its mirror j, prefetching the
+# second one's Q and first key tile while the first finishes.  These shapes
+# take that path with an even and an odd tile count, ragged tails and Nq != Nk.
+PAIRED = [
+    # B, H, Nq, Nk, d
+    (2, 64, 2000, 2000, 128),     # 16 query tiles, ragged 80-row tail
+    (2, 70, 1900, 1900, 64),      # 15 query tiles: the middle one runs alone
+    (1, 256, 1000, 1300, 64),     # Nk > Nq (bottom-right causal alignment)
+    (1, 256, 1100, 900, 128),     # Nq > Nk: leading rows see no key
+]
+
+
+@pytest.mark.parametrize("case", PAIRED, ids=lambda c: "-".join(map(str, c)))
+def test_paired_query_tiles_sampled_heads(case):
+    B, H, Nq, Nk, d = case
+    assert B * H * ((Nq + 127) // 128) >= 2048   # the paired path
+    banner(f"fwd paired {case}")
+    q, k, v = wl.make_inputs(B, H, Nq, Nk, d, "bf16", seed=900 + Nq + Nk + d)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = gpu_fwd(q, k, v, scale, True)
+    g = torch.Generator().manual_seed(Nq * 7 + Nk)
+    heads = [0, B * H - 1] + torch.randperm(B * H, generator=g)[:3].tolist()
+    for bh in heads:
+        b, h = divmod(bh, H)
+        o_ref, lse_ref = attention_forward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), scale, True)
+        check_forward(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, "bf16", f"{case} head {bh}")
+
+
 # ------------------------------------------------------------------ page pins
 def _pad_fp32(x, width):
     out = torch.zeros(x.shape[0], width, dtype=torch.float32)
