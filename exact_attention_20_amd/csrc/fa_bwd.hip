@@ -93,21 +93,33 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
     const int l32 = lane & 31, hg = lane >> 5;
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
     const int n_kt = (Nk + BKV - 1) / BKV;
-    int bh, kt;
-    map_head_tile(blockIdx.x, p.BH * n_kt, n_kt, bh, kt);   // ascending: heavy causal tiles first
-    const int k0 = kt * BKV;
-    const int kw = k0 + wave * 32;            // this wave's first key
-    const int kj = kw + l32;                  // this lane's key
+    // key tiles of this workgroup: j (ascending j = heavy causal tiles
+    // first), then with pairing its mirror n-1-j (equal causal work per
+    // workgroup)
+    int bh, slot;
+    map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, slot);
+    const int n_items = (p.kv_paired && slot != n_kt - 1 - slot) ? 2 : 1;
 
     const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
     const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
     const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
     const bf16* dOh = (const bf16*)p.dO + (size_t)bh * Nq * D;
 
-    // K^T and V^T as B operands: lane = key, 8 consecutive d per k-step
-    // (rows past Nk read as zero; their dK / dV are never written).
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (uint32_t)Nk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, (uint32_t)Nk * D * 2);
+    const TileCopy<D, BQ, 4> copier(wave, lane);
+    const i32x4 rq_w = make_rsrc_words(Qh, (uint32_t)Nq * D * 2);
+    const i32x4 rdo_w = make_rsrc_words(dOh, (uint32_t)Nq * D * 2);
+    const uint32_t smem_lds = lds_address(smem);
+
+    for (int it = 0; it < n_items; ++it) {
+    const int kt = it == 0 ? slot : n_kt - 1 - slot;
+    const int k0 = kt * BKV;
+    const int kw = k0 + wave * 32;            // this wave's first key
+    const int kj = kw + l32;                  // this lane's key
+
+    // K^T and V^T as B operands: lane = key, 8 consecutive d per k-step
+    // (rows past Nk read as zero; their dK / dV are never written).
     bf16x8 kreg[NKK], vreg[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -123,10 +135,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
     const int n_qt = (Nq + BQ - 1) / BQ;
     const int wq_first = CAUSAL ? kw - off : 0;   // first query that sees this wave's first key
 
-    const TileCopy<D, BQ, 4> copier(wave, lane);
-    const i32x4 rq_w = make_rsrc_words(Qh, (uint32_t)Nq * D * 2);
-    const i32x4 rdo_w = make_rsrc_words(dOh, (uint32_t)Nq * D * 2);
-    const uint32_t smem_lds = lds_address(smem);
     auto load_step = [&](int qt, int stage) {
         const uint32_t base = smem_lds + stage * STAGE;
         copier.issue(rq_w, qt * BQ, base);
@@ -260,6 +268,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
                 *(u32x2*)(dVr + dcol) = wv;
             }
     }
+    }   // items
 }
 
 // ---------------------------------------------------------------------------
@@ -281,25 +290,34 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     const int l32 = lane & 31, hg = lane >> 5;
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
     const int n_qt = (Nq + BQ - 1) / BQ;
-    int bh, qt;
-    map_head_tile(blockIdx.x, p.BH * n_qt, n_qt, bh, qt);
-    qt = n_qt - 1 - qt;                        // heavy causal tiles first
-    const int q0 = qt * BQ;
-    const int qw = q0 + wave * 32;
-    const int qi = qw + l32;
+    // query tiles of this workgroup: n-1-j (heavy causal tiles first), then
+    // with pairing its mirror j
+    int bh, slot;
+    map_head_tile(blockIdx.x, p.BH * p.q_slots, p.q_slots, bh, slot);
+    const int n_items = (p.q_paired && slot != n_qt - 1 - slot) ? 2 : 1;
 
     const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
     const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
     const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
     const bf16* dOh = (const bf16*)p.dO + (size_t)bh * Nq * D;
 
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, (uint32_t)Nq * D * 2);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dOh, (uint32_t)Nq * D * 2);
+    const TileCopy<D, BC, 4> copier(wave, lane);
+    const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
+    const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
+    const uint32_t smem_lds = lds_address(smem);
+
+    for (int it = 0; it < n_items; ++it) {
+    const int qt = it == 0 ? n_qt - 1 - slot : slot;
+    const int q0 = qt * BQ;
+    const int qw = q0 + wave * 32;
+    const int qi = qw + l32;
     const int kend = CAUSAL ? min(Nk, q0 + BQ + off) : Nk;
     const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
     const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
 
     // this lane's query: Q and dO as B operands, its LSE2 and D
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, (uint32_t)Nq * D * 2);
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dOh, (uint32_t)Nq * D * 2);
     bf16x8 qreg[NKK], doreg[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -313,10 +331,6 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
         dd = p.dvec[(size_t)bh * Nq + qi];
     }
 
-    const TileCopy<D, BC, 4> copier(wave, lane);
-    const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
-    const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
-    const uint32_t smem_lds = lds_address(smem);
     auto load_tile = [&](int k0, int buf) {
         copier.issue(rk_w, k0, smem_lds + buf * BUF_BYTES);
         copier.issue(rv_w, k0, smem_lds + buf * BUF_BYTES + T_BYTES);
@@ -400,6 +414,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
                 *(u32x2*)(dQr + db * 32 + g * 8 + 4 * hg) = w;
             }
     }
+    }   // items
 }
 
 // ---------------------------------------------------------------------------
@@ -421,13 +436,13 @@ static hipError_t launch_bwd_d(bool causal, const BwdParams& p, hipStream_t s) {
     }
     BwdParams pp = p;
     void* args[] = {&pp};
-    const long grid_kv = (long)p.BH * ((p.Nk + 127) / 128);
+    const long grid_kv = (long)p.BH * p.kv_slots;
     if (grid_kv > 0) {   // with Nq == 0 the walk is empty and dK = dV = 0 are written
         const void* fn = causal ? (const void*)bwd_dkdv_kernel<D, true> : (const void*)bwd_dkdv_kernel<D, false>;
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
-    const long grid_q = (long)p.BH * ((p.Nq + 127) / 128);
+    const long grid_q = (long)p.BH * p.q_slots;
     if (grid_q > 0) {   // with Nk == 0 every row is empty and dQ = 0 is written
         const void* fn = causal ? (const void*)bwd_dq_kernel<D, true> : (const void*)bwd_dq_kernel<D, false>;
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_q), dim3(256), args, 0, s);

@@ -37,6 +37,10 @@ struct BwdParams {
     int Nq;
     int Nk;
     int BH;
+    int kv_slots;      // dK/dV workgroups per (batch, head): 128-key tiles, halved when paired
+    int kv_paired;
+    int q_slots;       // dQ workgroups per (batch, head): 128-query tiles, halved when paired
+    int q_paired;
     float scale;
     float scale_log2;
 };

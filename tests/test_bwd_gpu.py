@@ -54,6 +54,34 @@ def test_backward_small_and_ragged(case):
     check_grad(to64(dv), rv, f"dv {case}")
 
 
+# Large causal grids take the paired path in both backward kernels (a
+# workgroup runs key tile j then n-1-j, query tile n-1-j then j): odd tile
+# counts, ragged tails and Nq != Nk.
+PAIRED = [
+    # B, H, Nq, Nk, d
+    (2, 70, 1900, 1900, 64),      # 15 key tiles and 15 query tiles of 128
+    (1, 256, 1000, 1300, 64),     # Nk > Nq
+    (1, 256, 1300, 1000, 128),    # Nq > Nk: leading rows see no key
+]
+
+
+@pytest.mark.parametrize("case", PAIRED, ids=lambda c: "-".join(map(str, c)))
+def test_backward_paired_tiles_sampled_heads(case):
+    B, H, Nq, Nk, d = case
+    assert B * H * ((min(Nq, Nk) + 127) // 128) >= 2048   # both kernels pair
+    banner(f"bwd paired {case}")
+    q, k, v, do = wl.make_inputs(B, H, Nq, Nk, d, "bf16", seed=700 + Nq + Nk + d, with_do=True)
+    scale = 1.0 / np.sqrt(d)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, scale, True)
+    for bh in (0, B * H // 2, B * H - 1):
+        b, h = divmod(bh, H)
+        rq, rk, rv, *_ = attention_backward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]),
+                                            to64(do[b, h]), scale, True)
+        check_grad(to64(dq[b, h]), rq, f"dq {case} head {bh}")
+        check_grad(to64(dk[b, h]), rk, f"dk {case} head {bh}")
+        check_grad(to64(dv[b, h]), rv, f"dv {case} head {bh}")
+
+
 def test_train_step_workload_sampled_heads():
     w = wl.TRAIN_STEP
     banner(w.describe())
