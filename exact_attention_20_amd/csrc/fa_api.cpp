@@ -53,7 +53,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
     p.Nq = Nq;
     p.Nk = Nk;
     p.n_qtiles = n_qtiles;
-    p.paired = fa::fwd_pair_tiles(dtype, causal != 0, BH, n_qtiles) ? 1 : 0;
+    p.paired = fa::fwd_pair_tiles(dtype, d, causal != 0, BH, n_qtiles) ? 1 : 0;
     p.n_slots = p.paired ? (n_qtiles + 1) / 2 : n_qtiles;
     p.total_wg = (int)(BH * p.n_slots);
     p.scale_log2 = scale * 1.44269504088896340736f;
@@ -104,9 +104,9 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
     p.Nk = Nk;
     p.BH = (int)BH;
     const int n_kt = (Nk + 127) / 128, n_qt = (Nq + 127) / 128;
-    p.kv_paired = fa::fwd_pair_tiles(dtype, causal != 0, BH, n_kt) ? 1 : 0;
+    p.kv_paired = fa::bwd_pair_tiles(causal != 0, BH, n_kt) ? 1 : 0;
     p.kv_slots = p.kv_paired ? (n_kt + 1) / 2 : n_kt;
-    p.q_paired = fa::fwd_pair_tiles(dtype, causal != 0, BH, n_qt) ? 1 : 0;
+    p.q_paired = fa::bwd_pair_tiles(causal != 0, BH, n_qt) ? 1 : 0;
     p.q_slots = p.q_paired ? (n_qt + 1) / 2 : n_qt;
     p.scale = scale;
     p.scale_log2 = scale * 1.44269504088896340736f;

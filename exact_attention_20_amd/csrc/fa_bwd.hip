@@ -451,6 +451,13 @@ static hipError_t launch_bwd_d(bool causal, const BwdParams& p, hipStream_t s) {
     return hipSuccess;
 }
 
+// Pair mirrored tiles in the dK/dV and dQ kernels on large causal grids of
+// short sequences (every workgroup then does the same causal work; measured
+// +11% at N=4096 d=64, +2% at d=128).
+bool bwd_pair_tiles(bool causal, long bh, int n_tiles) {
+    return causal && n_tiles >= 2 && n_tiles <= 64 && bh * n_tiles >= 4 * 512;
+}
+
 hipError_t launch_bwd(int d, bool causal, BwdParams p, hipStream_t stream) {
     return d == 64 ? launch_bwd_d<64>(causal, p, stream) : launch_bwd_d<128>(causal, p, stream);
 }

@@ -412,12 +412,13 @@ int fwd_rows_per_workgroup(int dtype, int d) {
 }
 
 // 256 CUs x 2 resident workgroups = 512 slots; pair when the unpaired grid
-// covers them at least four times and sequences are short enough that a
-// workgroup's start-up (Q and first key tile from HBM) and epilogue are a
-// noticeable share of its work (measured: +10% at N=4096 d=64, none at
-// N=32768 d=128).
-bool fwd_pair_tiles(int dtype, bool causal, long bh, int n_qtiles) {
-    return dtype == 1 && causal && n_qtiles >= 2 && n_qtiles <= 64 && bh * n_qtiles >= 4 * 512;
+// covers them at least four times and a workgroup's start-up (Q and first key
+// tile from HBM) and epilogue are a noticeable share of its work: short
+// sequences with d = 64 (measured +10% at N=4096).  At d = 128 pairing gained
+// nothing at N=4096 and cost L2 locality (twice the heads in flight per XCD:
+// 1.4x the L2 miss traffic), and at N=32768 it lost 1.6%.
+bool fwd_pair_tiles(int dtype, int d, bool causal, long bh, int n_qtiles) {
+    return dtype == 1 && d == 64 && causal && n_qtiles >= 2 && n_qtiles <= 64 && bh * n_qtiles >= 4 * 512;
 }
 
 template <typename KernelT>

@@ -51,7 +51,9 @@ int fwd_rows_per_workgroup(int dtype, int d);
 // Whether the bf16 forward pairs query tiles (n-1-j with j) in one workgroup:
 // causal only, where it evens out the work, and only for grids large enough
 // that halving the workgroup count still fills the GPU several times over.
-bool fwd_pair_tiles(int dtype, bool causal, long bh, int n_qtiles);
+bool fwd_pair_tiles(int dtype, int d, bool causal, long bh, int n_qtiles);
+// The same decision for the backward kernels' key and query tiles.
+bool bwd_pair_tiles(bool causal, long bh, int n_tiles);
 
 hipError_t launch_fwd(int dtype, int d, bool causal, int BH, FwdParams p, hipStream_t stream);
 hipError_t launch_bwd(int d, bool causal, BwdParams p, hipStream_t stream);

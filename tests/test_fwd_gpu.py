@@ -116,16 +116,19 @@ def test_train_step_forward_sampled_rows():
 
 
 # ------------------------------------------ paired query tiles (large causal grids)
-# With causal masking and at least 2048 (batch*head, 128-row query tile) units,
-# a bf16 workgroup runs query tile n-1-j and then its mirror j, prefetching the
-# second one's Q and first key tile while the first finishes.  These shapes
-# take that path with an even and an odd tile count, ragged tails and Nq != Nk.
+# With causal masking, d = 64, at most 64 query tiles per head and at least
+# 2048 (batch*head, 128-row query tile) units, a bf16 workgroup runs query tile
+# n-1-j and then its mirror j, prefetching the second one's Q and first key
+# tile while the first finishes.  These shapes take that path with an even and
+# an odd tile count, ragged tails and Nq != Nk; the last one is the same kind
+# of grid at d = 128, which does not pair.
 PAIRED = [
     # B, H, Nq, Nk, d
-    (2, 64, 2000, 2000, 128),     # 16 query tiles, ragged 80-row tail
+    (2, 64, 2000, 2000, 64),      # 16 query tiles, ragged 80-row tail
     (2, 70, 1900, 1900, 64),      # 15 query tiles: the middle one runs alone
     (1, 256, 1000, 1300, 64),     # Nk > Nq (bottom-right causal alignment)
-    (1, 256, 1100, 900, 128),     # Nq > Nk: leading rows see no key
+    (1, 256, 1100, 900, 64),      # Nq > Nk: leading rows see no key
+    (2, 64, 2000, 2000, 128),     # unpaired at d = 128
 ]
 
 
