@@ -1,7 +1,7 @@
 """Throughput of the fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-train-step] [--cold]
 
 A step is one fa_fwd launch over the whole workload (default: B=4 H=32
 N=4096 d=128 bf16 causal, LSE saved), with Q, K, V already resident in device
@@ -12,8 +12,13 @@ Throughput is causal-adjusted: 4*d FLOPs per visible (query, key) pair.
 Prints ONE JSON line.  ``roofline`` compares the kernel against MI355X's
 published dense bf16 MFMA peak (2.5 PFLOP/s); ``traffic`` is taken from the
 committed rocprofv3 counter summary when it was measured on the current kernel
-source, else null.  ``cpu_baseline`` times the fp64 oracle on a bounded sample
-of the same workload on the host cores.
+source, else null.  ``hbm`` gives the algorithmic bytes (read Q, K, V once,
+write O and LSE) per launch and the rate they are moved at; ``cold`` (with
+--cold, and always for the short-sequence GPT-2-shaped workload) repeats the
+timing one launch at a time after flushing L2 and the Infinity Cache.
+``train_step`` times fa_fwd and fa_bwd on the training-step workload.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
 """
 
 from __future__ import annotations
@@ -49,6 +54,13 @@ def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
 
 def fwd_flops(w) -> int:
     return 4 * w.d * visible_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
+
+
+def algorithmic_bytes(w) -> int:
+    """Compulsory HBM bytes of one forward launch: read Q, K, V once, write O
+    and the fp32 LSE."""
+    esz = 2 if w.dtype == "bf16" else 4
+    return w.B * w.H * ((2 * w.Nq + 2 * w.Nk) * w.d * esz + 4 * w.Nq)
 
 
 def kernel_source_hash() -> str:
@@ -215,6 +227,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train-step", action="store_true",
                     help="skip the forward+backward timing on the training-step workload")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time launches one by one after flushing L2 and the Infinity Cache "
+                         "(a 512 MiB write before each); on by default for the short-sequence "
+                         "GPT-2-shaped workload, whose inputs fit in the Infinity Cache")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -284,6 +300,7 @@ def main():
     peak = PEAK[w.dtype]
 
     traffic = traffic_for(w.name)
+    nbytes = algorithmic_bytes(w)
     result = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -301,7 +318,27 @@ def main():
                    "causal": w.causal, "lse_saved": True, "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
+        "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "peak_GBps": 8000.0, "note": "algorithmic bytes / launch time, warm caches"},
     }
+    if args.cold or w.name == "gpt2_small_bf16":
+        # L2 (4 MiB per XCD) and the 256 MiB Infinity Cache are flushed by a
+        # 512 MiB write before every launch; each launch is timed on its own.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(max(10, args.steps // 2)):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        cms = times[len(times) // 2]
+        result["cold"] = {"ms_median": round(cms, 5), "tflops": round(flops / (cms * 1e-3) / 1e12, 3),
+                          "achieved_GBps": round(nbytes / (cms * 1e-3) / 1e9, 1), "launches": len(times),
+                          "note": "L2 and Infinity Cache flushed before each launch"}
     if not args.no_train_step:
         result["train_step"] = train_step_timing(fa, wl, steps=20, warmup=5)
     if not args.no_cpu_baseline:

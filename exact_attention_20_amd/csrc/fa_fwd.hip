@@ -176,14 +176,16 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
             // ---- mask: only tiles that straddle the diagonal or the tail ----
             const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw + off);
             if (need_mask) {
+                // item i of block kb is key k0 + kb*32 + (i/4)*8 + 4*hg + i%4: it is
+                // visible iff its offset within the tile, past 4*hg, is <= lim
+                // (key < Nk and, causal, key <= qi + off): one compare per item
+                int lim = Nk - 1 - k0 - 4 * hg;
+                if (CAUSAL) lim = min(lim, qi + off - k0 - 4 * hg);
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + kb * 32 + (i >> 2) * 8 + 4 * hg + (i & 3);
-                        const bool vis = key < Nk && (!CAUSAL || key <= qi + off);
-                        if (!vis) s[kb][i] = -INFINITY;
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) s[kb][i] = -INFINITY;
             }
             // ---- online softmax update (base-2, scale folded) ----
             // m_run is the scaling base.  It moves (and O, l are rescaled by
