@@ -284,6 +284,21 @@ def main():
         if st != 0:
             raise fa.FAError(st, "fa_fwd")
 
+    # Decoding (a few query rows against a long key range) runs the split-KV
+    # path: it is HBM-bound, so its roofline is the 8 TB/s HBM peak.
+    decode = w.name == "decode_bf16"
+    unsplit_ms = None
+    if decode:
+        unsplit_ms = time_launches(step, stream, max(5, args.steps // 5), 3)
+        need = fa.fa_fwd_splitkv_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, dtype_code, 0)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        sargv = argv[:13] + (0, ws.data_ptr(), need, sh)
+
+        def step():  # noqa: F811
+            st = fa.fa_fwd_splitkv(*sargv)
+            if st != 0:
+                raise fa.FAError(st, "fa_fwd_splitkv")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -321,6 +336,16 @@ def main():
         "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "peak_GBps": 8000.0, "note": "algorithmic bytes / launch time, warm caches"},
     }
+    if decode:
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        result["metric"] = "attention decode (split-KV) HBM GB/s, 1xMI355X"
+        result["value"] = round(gbps, 1)
+        result["unit"] = "GB/s"
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
+                              "frac": round(gbps / 8000.0, 4), "traffic": traffic}
+        result["decode"] = {"path": "fa_fwd_splitkv, automatic run count", "unsplit_fa_fwd_ms": round(unsplit_ms, 5),
+                            "unsplit_GBps": round(nbytes / (unsplit_ms * 1e-3) / 1e9, 1),
+                            "tflops": round(tflops, 3)}
     if args.cold or w.name == "gpt2_small_bf16":
         # L2 (4 MiB per XCD) and the 256 MiB Infinity Cache are flushed by a
         # 512 MiB write before every launch; each launch is timed on its own.

@@ -7,6 +7,9 @@ library is missing, every call raises -- there is no fallback path.
 
 Raw entry points, same names and argument order as ``include/fa.h``:
     fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, stream) -> int
+    fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, n_splits,
+                   workspace, workspace_bytes, stream) -> int
+    fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, n_splits) -> int
     fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal,
            dtype, workspace, workspace_bytes, stream) -> int
     fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) -> int
@@ -16,6 +19,7 @@ Raw entry points, same names and argument order as ``include/fa.h``:
 Tensor helpers that allocate the outputs with torch and raise ``FAError`` on a
 non-zero status:
     attention_forward(q, k, v, scale=None, causal=False) -> (o, lse)
+    attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0) -> (o, lse)
     attention_backward(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
 """
 
@@ -27,8 +31,9 @@ import os
 
 __all__ = [
     "FA_F32", "FA_BF16", "FAError", "library_path", "load_library",
-    "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror",
-    "attention_forward", "attention_backward",
+    "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
+    "fa_bwd_workspace_bytes", "fa_strerror",
+    "attention_forward", "attention_forward_splitkv", "attention_backward",
 ]
 
 FA_F32 = 0
@@ -62,6 +67,10 @@ def load_library() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -79,6 +88,17 @@ def _p(x):
 def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, stream) -> int:
     return load_library().fa_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Nq, Nk, d,
                                  float(scale), int(causal), int(dtype), _p(stream))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, n_splits,
+                   workspace, workspace_bytes, stream) -> int:
+    return load_library().fa_fwd_splitkv(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Nq, Nk, d,
+                                         float(scale), int(causal), int(dtype), int(n_splits),
+                                         _p(workspace), int(workspace_bytes), _p(stream))
+
+
+def fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, n_splits) -> int:
+    return int(load_library().fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, n_splits))
 
 
 def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype,
@@ -150,6 +170,33 @@ def attention_forward(q, k, v, scale=None, causal=False, out=None, lse=None, wan
                 causal, _dtype_code(q), _stream())
     if st != 0:
         raise FAError(st, "fa_fwd")
+    return out, lse
+
+
+def attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0, workspace=None):
+    """attention_forward through fa_fwd_splitkv (bf16 only): the key range of
+    each query tile is split over several workgroups whose partial results are
+    merged by their LSE.  n_splits = 0 lets the library choose."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dt = q.dtype
+    _check(q, "q", (B, H, Nq, d), dt)
+    _check(k, "k", (B, H, Nk, d), dt)
+    _check(v, "v", (B, H, Nk, d), dt)
+    code = _dtype_code(q)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, code, n_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, Nq, Nk, d, scale, causal, code, n_splits,
+                        workspace.data_ptr() if workspace is not None else 0,
+                        workspace.numel() if workspace is not None else 0, _stream())
+    if st != 0:
+        raise FAError(st, "fa_fwd_splitkv")
     return out, lse
 
 

@@ -44,7 +44,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
 
     const int br = fa::fwd_rows_per_workgroup(dtype, d);
     const int n_qtiles = (Nq + br - 1) / br;
-    fa::FwdParams p;
+    fa::FwdParams p = {};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -58,6 +58,95 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
     p.total_wg = (int)(BH * p.n_slots);
     p.scale_log2 = scale * 1.44269504088896340736f;
     return hip_status(fa::launch_fwd(dtype, d, causal != 0, (int)BH, p, (hipStream_t)stream));
+}
+
+namespace {
+
+// Runs of 64-key tiles for the split-KV forward.  n_splits = 0 asks for
+// enough workgroups to cover the GPU's 512 resident slots four times (at
+// least 4 key tiles per run); the effective count is ceil(tiles / per_run).
+struct SplitPlan {
+    int n_qtiles, n_splits, tiles_per_split;
+};
+
+SplitPlan plan_split(long BH, int Nq, int Nk, int n_splits) {
+    SplitPlan sp;
+    sp.n_qtiles = (Nq + 127) / 128;
+    const int n_kt = Nk > 0 ? (Nk + 63) / 64 : 1;
+    int want = n_splits;
+    if (want == 0) {
+        const long units = BH * sp.n_qtiles;
+        const long target = (2048 + units - 1) / units;
+        const int cap = n_kt / 4 > 1 ? n_kt / 4 : 1;
+        want = (int)(target < cap ? target : cap);
+        if (want < 1) want = 1;
+    }
+    if (want > n_kt) want = n_kt;
+    sp.tiles_per_split = (n_kt + want - 1) / want;
+    sp.n_splits = (n_kt + sp.tiles_per_split - 1) / sp.tiles_per_split;
+    return sp;
+}
+
+size_t split_part_bytes(long BH, int Nq, int d, int n_splits, size_t* lse_off) {
+    const size_t rows = (size_t)n_splits * BH * Nq;
+    const size_t obytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+    const size_t lbytes = (rows * sizeof(float) + 255) & ~(size_t)255;
+    if (lse_off) *lse_off = obytes;
+    return obytes + lbytes;
+}
+
+}  // namespace
+
+extern "C" size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int n_splits) {
+    if (check_common(B, H, Nq, Nk, d, 1.0f, dtype) != FA_OK) return 0;
+    if (dtype != FA_BF16 || n_splits < 0 || n_splits > FA_MAX_SPLITS) return 0;
+    const long BH = (long)B * H;
+    if (BH == 0 || Nq == 0) return 0;
+    const SplitPlan sp = plan_split(BH, Nq, Nk, n_splits);
+    return split_part_bytes(BH, Nq, d, sp.n_splits, nullptr);
+}
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                              int dtype, int n_splits, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    int st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (n_splits < 0 || n_splits > FA_MAX_SPLITS) return FA_ERR_SHAPE;
+    const long BH = (long)B * H;
+    if (BH == 0 || Nq == 0) return FA_OK;
+    if (!q || !o || (Nk > 0 && (!k || !v))) return FA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(o) || (Nk > 0 && (!aligned16(k) || !aligned16(v)))) return FA_ERR_ALIGN;
+    if (lse && !aligned4(lse)) return FA_ERR_ALIGN;
+    const SplitPlan sp = plan_split(BH, Nq, Nk, n_splits);
+    size_t lse_off = 0;
+    const size_t need = split_part_bytes(BH, Nq, d, sp.n_splits, &lse_off);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    // one workgroup per (head, query tile, run), then one per output row
+    if ((long double)BH * sp.n_qtiles * sp.n_splits > 2.0e9L || (long double)BH * Nq > 2.0e9L)
+        return FA_ERR_SHAPE;
+
+    fa::FwdParams p = {};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.n_qtiles = sp.n_qtiles;
+    p.n_slots = sp.n_qtiles;
+    p.paired = 0;
+    p.total_wg = (int)(BH * sp.n_qtiles * sp.n_splits);
+    p.scale_log2 = scale * 1.44269504088896340736f;
+    p.BH = (int)BH;
+    p.n_splits = sp.n_splits;
+    p.tiles_per_split = sp.tiles_per_split;
+    p.o_part = (float*)workspace;
+    p.lse_part = (float*)((char*)workspace + lse_off);
+    return hip_status(fa::launch_fwd_split(d, causal != 0, p, (hipStream_t)stream));
 }
 
 extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {

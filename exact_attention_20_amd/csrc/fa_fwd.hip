@@ -52,7 +52,12 @@ __device__ __forceinline__ void map_workgroup(int w, int total, int n_qtiles, in
 // and l are rescaled: P values stay <= 2^8, far inside bf16 and fp32 range.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, bool CAUSAL>
+// SPLIT: split-KV mode.  The key tiles of each query tile are divided into
+// p.n_splits runs of p.tiles_per_split tiles, one workgroup per (batch*head,
+// query tile, run); each writes its normalised partial O (fp32) and partial
+// LSE (log2 units) to p.o_part / p.lse_part, and fwd_combine_kernel merges
+// them.  Without SPLIT the workgroup owns whole query tiles.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     constexpr int BR = 128, BC = 64;
     constexpr int NKK = D / 16;        // k-steps over d for S^T
@@ -71,10 +76,17 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     // The workgroup's query tiles: tile n-1-j, then with pairing its mirror
     // j of the same head (causal: the two tiles together see n+1 rows of key
     // tiles whatever j is, so every workgroup gets the same work).
-    int bh, slot;
-    map_head_tile(blockIdx.x, p.total_wg, p.n_slots, bh, slot);
+    int bh, slot, split = 0;
     const int nqt = p.n_qtiles;
-    const int n_items = (p.paired && slot != nqt - 1 - slot) ? 2 : 1;
+    if (SPLIT) {
+        int r;
+        map_head_tile(blockIdx.x, p.total_wg, nqt * p.n_splits, bh, r);
+        slot = nqt - 1 - r / p.n_splits;   // so that tile n-1-slot is tile r / n_splits
+        split = r % p.n_splits;
+    } else {
+        map_head_tile(blockIdx.x, p.total_wg, p.n_slots, bh, slot);
+    }
+    const int n_items = (!SPLIT && p.paired && slot != nqt - 1 - slot) ? 2 : 1;
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
     const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
     const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
@@ -118,8 +130,12 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     const int q0 = qt * BR;
     const int qw = q0 + wave * 32;     // this wave's first query
     const int qi = qw + l32;           // this lane's query
-    const int ntiles = tiles_of(qt);
-    const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;   // last key + 1 this wave sees
+    // key tiles [t_lo, t_hi) of this item (a run of them in split-KV mode)
+    const int t_lo = SPLIT ? split * p.tiles_per_split : 0;
+    const int t_hi = SPLIT ? min(tiles_of(qt), t_lo + p.tiles_per_split) : tiles_of(qt);
+    const int ntiles = t_hi > t_lo ? t_hi - t_lo : 0;
+    // last key + 1 this wave sees; a wave whose rows all lie past Nq skips the math
+    const int kend_w = qw >= Nq ? 0 : CAUSAL ? min(Nk, qw + 32 + off) : Nk;
     const bool more = it + 1 < n_items;
     const int next_ntiles = more ? tiles_of(slot) : 0;
 
@@ -132,7 +148,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
 
     if (!prefetched) {
         load_q(qi);
-        if (ntiles > 0) load_tile(0, b0);
+        if (ntiles > 0) load_tile(t_lo * BC, b0);
         // vmcnt(0) through the builtin so the compiler also knows Q is resident
         // (and adds no Q waits inside the loop, where they would stall on the
         // in-flight copies); the hardware counter covers the tile copies too.
@@ -140,14 +156,14 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
         tile_barrier();
     }
 
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = t_lo; t < t_hi; ++t) {
         const int k0 = t * BC;
-        const int buf = (b0 + t) & 1;
+        const int buf = (b0 + t - t_lo) & 1;
         const char* kbuf = smem + buf * BUF_BYTES;
         const char* vbuf = kbuf + T_BYTES;
         // the other buffer takes the next key tile, or the next item's first
-        const bool has_next = t + 1 < ntiles || next_ntiles > 0;
-        if (t + 1 < ntiles) load_tile(k0 + BC, buf ^ 1);
+        const bool has_next = t + 1 < t_hi || next_ntiles > 0;
+        if (t + 1 < t_hi) load_tile(k0 + BC, buf ^ 1);
         else if (has_next) load_tile(0, buf ^ 1);
 
         if (k0 < kend_w) {
@@ -261,6 +277,25 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l) ----
     const float l_tot = xhalf_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (SPLIT) {
+        // partial result of this run of key tiles: O_s = O~ / l (fp32) and
+        // LSE_s = m + log2 l (log2 units; -inf when the run saw no key)
+        if (qi < Nq) {
+            const size_t row = ((size_t)split * p.BH + bh) * Nq + qi;
+            float* Op = p.o_part + row * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * g + e] * inv;
+                    *(f32x4*)(Op + db * 32 + g * 8 + 4 * hg) = w;
+                }
+            if (hg == 0) p.lse_part[row] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+        }
+        continue;
+    }
     if (qi < Nq) {
         bf16* Oh = (bf16*)p.o + (size_t)bh * Nq * D + (size_t)qi * D;
 #pragma unroll
@@ -277,6 +312,70 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     }
     }   // items
 }
+// ---------------------------------------------------------------------------
+// Split-KV combine: the partial results (O_s, L_s) of a row over disjoint key
+// runs merge by the online-softmax rescale ("01 · IO-awareness、online
+// softmax 与 tiling" §2: the update is order-insensitive):
+//   M = max_s L_s,  w_s = 2^(L_s - M),  O = sum_s w_s O_s / sum_s w_s,
+//   LSE = ln2 * (M + log2 sum_s w_s).
+// A row no run saw (every L_s = -inf) gets O = 0, LSE = -inf.
+// One workgroup of 256 threads per row: thread t owns 8 output columns
+// (chunk t % (D/8)) of the runs s = t / (D/8), + 256 / (D/8), ...; the
+// partial sums are then added across the run lanes through LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) fwd_combine_kernel(FwdParams p) {
+    constexpr int TPR = D / 8;          // 8-column chunks per row
+    constexpr int J = 256 / TPR;        // run lanes
+    __shared__ float red[J][D + 4];
+    __shared__ float wred[4];
+    const long rows = (long)p.BH * p.Nq;
+    const long row = blockIdx.x;
+    const int t = threadIdx.x, c = t % TPR, j = t / TPR;
+    const int ns = p.n_splits;
+    // M = max over the runs: strided over all 256 threads, then reduced
+    float M = -INFINITY;
+    for (int s = t; s < ns; s += 256) M = fmaxf(M, p.lse_part[(size_t)s * rows + row]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if ((t & 63) == 0) wred[t >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    float wsum = 0.f;
+    if (M != -INFINITY) {
+        for (int s = j; s < ns; s += J) {
+            const float L = p.lse_part[(size_t)s * rows + row];
+            if (L == -INFINITY) continue;
+            const float w = exp2_hw(L - M);
+            wsum += w;
+            const float* Op = p.o_part + ((size_t)s * rows + row) * D + c * 8;
+            const f32x4 a = *(const f32x4*)Op;
+            const f32x4 b = *(const f32x4*)(Op + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] = fmaf(w, a[e], acc[e]);
+                acc[4 + e] = fmaf(w, b[e], acc[4 + e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[j][c * 8 + e] = acc[e];
+    if (c == 0) red[j][D] = wsum;
+    __syncthreads();
+    if (t < D) {
+        float o = 0.f, ws = 0.f;
+        for (int jj = 0; jj < J; ++jj) {
+            o += red[jj][t];
+            ws += red[jj][D];
+        }
+        ((bf16*)p.o)[row * D + t] = (bf16)(ws > 0.f ? o / ws : 0.f);
+        if (t == 0 && p.lse) p.lse[row] = ws > 0.f ? (M + __log2f(ws)) * kLn2 : -INFINITY;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 inputs and output: true fp32 products on the 32x32x2 fp32 MFMA.
 // BR = BC = 64 (2 waves x 32 rows); single-buffered LDS.
@@ -435,15 +534,30 @@ hipError_t launch_fwd(int dtype, int d, bool causal, int BH, FwdParams p, hipStr
     (void)BH;
     if (grid == 0) return hipSuccess;
     if (dtype == 1) {
-        if (d == 64) return causal ? launch(fwd_bf16_kernel<64, true>, grid, 256, p, stream)
-                                   : launch(fwd_bf16_kernel<64, false>, grid, 256, p, stream);
-        return causal ? launch(fwd_bf16_kernel<128, true>, grid, 256, p, stream)
-                      : launch(fwd_bf16_kernel<128, false>, grid, 256, p, stream);
+        if (d == 64) return causal ? launch(fwd_bf16_kernel<64, true, false>, grid, 256, p, stream)
+                                   : launch(fwd_bf16_kernel<64, false, false>, grid, 256, p, stream);
+        return causal ? launch(fwd_bf16_kernel<128, true, false>, grid, 256, p, stream)
+                      : launch(fwd_bf16_kernel<128, false, false>, grid, 256, p, stream);
     }
     if (d == 64) return causal ? launch(fwd_f32_kernel<64, true>, grid, 128, p, stream)
                                : launch(fwd_f32_kernel<64, false>, grid, 128, p, stream);
     return causal ? launch(fwd_f32_kernel<128, true>, grid, 128, p, stream)
                   : launch(fwd_f32_kernel<128, false>, grid, 128, p, stream);
+}
+
+hipError_t launch_fwd_split(int d, bool causal, FwdParams p, hipStream_t stream) {
+    if (p.total_wg == 0) return hipSuccess;
+    hipError_t e;
+    if (d == 64)
+        e = causal ? launch(fwd_bf16_kernel<64, true, true>, p.total_wg, 256, p, stream)
+                   : launch(fwd_bf16_kernel<64, false, true>, p.total_wg, 256, p, stream);
+    else
+        e = causal ? launch(fwd_bf16_kernel<128, true, true>, p.total_wg, 256, p, stream)
+                   : launch(fwd_bf16_kernel<128, false, true>, p.total_wg, 256, p, stream);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)((long)p.BH * p.Nq);
+    return d == 64 ? launch(fwd_combine_kernel<64>, grid, 256, p, stream)
+                   : launch(fwd_combine_kernel<128>, grid, 256, p, stream);
 }
 
 }  // namespace fa

@@ -18,8 +18,14 @@ struct FwdParams {
     int n_qtiles;      // ceil(Nq / BR) for the chosen kernel
     int n_slots;       // workgroups per (batch, head): n_qtiles, or ceil(n_qtiles / 2) when paired
     int paired;        // bf16 kernel: a workgroup runs query tiles n-1-j and j of one head
-    int total_wg;      // B * H * n_slots
+    int total_wg;      // B * H * n_slots (split-KV: B * H * n_qtiles * n_splits)
     float scale_log2;  // scale * log2(e)
+    // split-KV mode only
+    int BH;
+    int n_splits;         // runs of key tiles per query tile
+    int tiles_per_split;  // 64-key tiles per run
+    float* o_part;        // [n_splits, B*H, Nq, d] fp32 partial outputs
+    float* lse_part;      // [n_splits, B*H, Nq] fp32 partial LSE, log2 units
 };
 
 struct BwdParams {
@@ -56,6 +62,8 @@ bool fwd_pair_tiles(int dtype, int d, bool causal, long bh, int n_qtiles);
 bool bwd_pair_tiles(bool causal, long bh, int n_tiles);
 
 hipError_t launch_fwd(int dtype, int d, bool causal, int BH, FwdParams p, hipStream_t stream);
+// bf16 split-KV forward: partial kernel, then the combine kernel.
+hipError_t launch_fwd_split(int d, bool causal, FwdParams p, hipStream_t stream);
 hipError_t launch_bwd(int d, bool causal, BwdParams p, hipStream_t stream);
 
 }  // namespace fa

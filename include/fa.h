@@ -90,6 +90,38 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int dtype, void* stream);
 
 /*
+ * Split-KV forward ("01 · IO-awareness、online softmax 与 tiling" §2: the
+ * online update is order-insensitive, so partial results over disjoint key
+ * ranges merge exactly by rescaling).  Same inputs, outputs and semantics as
+ * fa_fwd, for grids too small to fill the GPU -- decoding, where Nq is a few
+ * rows and Nk is long.  The 64-key tiles each 128-row query tile sees are
+ * divided into runs, one workgroup per (batch, head, query tile, run); each
+ * writes its normalised partial O (fp32) and partial LSE into the workspace,
+ * and a second kernel merges them:
+ *     M = max_s L_s,  w_s = 2^(L_s - M),  O = sum w_s O_s / sum w_s,
+ *     LSE = ln2 * (M + log2 sum w_s).
+ *
+ *   n_splits  runs per query tile, 1..FA_MAX_SPLITS, or 0 to let the library
+ *             choose (enough workgroups to cover the GPU about four times over,
+ *             at least 4 key tiles per run).  The effective count is
+ *             ceil(T / ceil(T / n_splits)) for T = ceil(Nk / 64) key tiles.
+ *   workspace device memory of at least fa_fwd_splitkv_workspace_bytes() for
+ *             the same arguments; contents on entry ignored, on exit
+ *             unspecified.  Calls that share a workspace must not overlap.
+ *
+ * Only FA_BF16 (FA_ERR_DTYPE otherwise).  Deterministic.  Rounding differs
+ * from fa_fwd (the partials are merged in fp32), within the same tolerance.
+ */
+#define FA_MAX_SPLITS 1024
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int n_splits);
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   int dtype, int n_splits, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for these sizes: two float32 row
  * vectors [B,H,Nq] (the LSE in base-2 units and D = rowsum(dO * O)), each
  * rounded up to 256 bytes.  Returns 0 for invalid sizes or dtype.

@@ -35,7 +35,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
-    assert set(syms) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror"}
+    assert set(syms) == {"fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
+                         "fa_bwd_workspace_bytes", "fa_strerror"}
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -120,3 +121,43 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_PKG", str(tmp_path))
     with pytest.raises(RuntimeError, match="no fallback"):
         fa.load_library()
+
+
+def split(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=1, Nk=1000, d=128,
+             scale=0.088, causal=1, dtype=fa.FA_BF16, n_splits=4, workspace=FAKE,
+             workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_splitkv(**a)
+
+
+def test_splitkv_workspace_plan():
+    # 1000 keys = 16 tiles of 64; 4 runs of 4 tiles; 2 heads x 1 row
+    n = fa.fa_fwd_splitkv_workspace_bytes(1, 2, 1, 1000, 128, fa.FA_BF16, 4)
+    assert n == 4096 + 256            # O parts 4*2*1*128*4 B, LSE parts 32 B -> 256
+    # 5 requested runs of 16 tiles -> 4 tiles per run -> 4 effective runs
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 1, 1000, 128, fa.FA_BF16, 5) == n
+    # more runs than tiles clamp to one tile per run
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 100, 64, fa.FA_BF16, 50) == 512 + 256
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 100, 64, fa.FA_F32, 2) == 0
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 100, 64, fa.FA_BF16, -1) == 0
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 1, 0, 100, 64, fa.FA_BF16, 2) == 0
+    # automatic choice: 8 heads x 1 row, 8192 keys = 128 tiles -> capped at 32 runs of 4
+    auto = fa.fa_fwd_splitkv_workspace_bytes(1, 8, 1, 8192, 64, fa.FA_BF16, 0)
+    assert auto == 32 * 8 * 64 * 4 + 1024
+
+
+def test_splitkv_validation_codes():
+    assert split(dtype=fa.FA_F32) == -4
+    assert split(n_splits=-1) == -2
+    assert split(n_splits=1025) == -2
+    assert split(d=96) == -3
+    assert split(scale=float("nan")) == -8
+    assert split(q=0) == -1
+    assert split(o=FAKE_MIS) == -5
+    assert split(workspace=0) == -6
+    need = fa.fa_fwd_splitkv_workspace_bytes(1, 2, 1, 1000, 128, fa.FA_BF16, 4)
+    assert split(workspace_bytes=need - 1) == -6
+    assert split(workspace=FAKE_MIS) == -5
+    assert split(B=0) == 0
+    assert split(Nq=0) == 0

@@ -50,7 +50,12 @@ LLAMA_CAUSAL = Workload("llama_causal_bf16", 4, 32, 4096, 4096, 128, "bf16", Tru
 LONG_CONTEXT = Workload("long_context_bf16", 1, 32, 32768, 32768, 128, "bf16", True, seed=1004)
 TRAIN_STEP = Workload("train_step_bf16", 4, 16, 4096, 4096, 64, "bf16", True, backward=True, seed=1005)
 
-ALL = [SINGLE_HEAD, GPT2_SMALL, LLAMA_CAUSAL, LONG_CONTEXT, TRAIN_STEP]
+# Decoding one new token of a single sequence against the long-context key
+# length (split-KV path; unsplit, its 32 query tiles would leave the GPU idle):
+# Nq = 1 with bottom-right causal alignment sees every key.
+DECODE = Workload("decode_bf16", 1, 32, 1, 32768, 128, "bf16", True, seed=1006)
+
+ALL = [SINGLE_HEAD, GPT2_SMALL, LLAMA_CAUSAL, LONG_CONTEXT, TRAIN_STEP, DECODE]
 
 
 def torch_dtype(name: str) -> torch.dtype:
