@@ -94,8 +94,6 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
 
     // Buffer resources over this head's Q, K and V: rows past Nq / Nk read as
     // zero, so ragged tails need no branches.
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, (uint32_t)Nq * D * 2);
-
     // The copies go through async_load_lds16 (invisible to the compiler's
     // wait analysis): with the builtin form the compiler waits for the copy
     // of tile t+1 before the first V read of tile t, which puts a full HBM /
@@ -110,12 +108,18 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
         copier.issue(rv_w, k0, smem_lds + buf * BUF_BYTES + T_BYTES);
     };
 
+    // Q takes the same route: the BR x D query tile (exactly one K + V
+    // buffer) is copied into whichever buffer is idle at the start of an
+    // item, then each wave reads its 32 rows into registers.  The kernel thus
+    // has no register loads from memory at all, so the compiler's wait
+    // analysis never sees a load in flight inside the key loop; there the
+    // hardware counter also counts the copies of the next key tile, and any
+    // wait it placed would stall every tile on them.
+    static_assert(BR * D * 2 == BUF_BYTES, "a query tile fills one K + V buffer");
+    const TileCopy<D, BR, 4> qcopier(wave, lane);
+    const i32x4 rq_w = make_rsrc_words(Qh, (uint32_t)Nq * D * 2);
+    auto load_q = [&](int q0_, int buf) { qcopier.issue(rq_w, q0_, smem_lds + buf * BUF_BYTES); };
     bf16x8 qreg[NKK];
-    auto load_q = [&](int qi_) {
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-            qreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rq, (uint32_t)qi_ * D * 2 + (16 * kk + 8 * hg) * 2, 0));
-    };
     // Key tiles a query tile needs: causal stops after the last key its last
     // query can see; tiles beyond are skipped entirely.
     auto tiles_of = [&](int qt_) {
@@ -146,15 +150,20 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     float l_run = 0.f;         // partial running sum over this lane's keys
     float nbase = 0.f;         // -m_run, or 0 while the row has seen no key (every term is then 0)
 
+    // Q into the idle buffer b0^1 (issued after the previous item's loop
+    // when that item prefetched this one's first key tile into b0)
     if (!prefetched) {
-        load_q(qi);
+        load_q(q0, b0 ^ 1);
         if (ntiles > 0) load_tile(t_lo * BC, b0);
-        // vmcnt(0) through the builtin so the compiler also knows Q is resident
-        // (and adds no Q waits inside the loop, where they would stall on the
-        // in-flight copies); the hardware counter covers the tile copies too.
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        tile_barrier();
     }
+    vmem_wait_all();
+    tile_barrier();
+    {
+        const char* qbuf = smem + (b0 ^ 1) * BUF_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = tile_read_row<D>(qbuf, wave * 32, kk, lane);
+    }
+    tile_barrier();   // every wave holds its Q rows before b0^1 takes the next key tile
 
     for (int t = t_lo; t < t_hi; ++t) {
         const int k0 = t * BC;
@@ -268,11 +277,12 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
         tile_barrier();
     }
 
-    // The next item's Q goes into the (now idle) Q registers while this
-    // item's epilogue runs; its first key tile is already in LDS.
+    // The next item's first key tile is already in LDS (buffer b0 below);
+    // its Q tile is copied into the other buffer, idle since the loop's last
+    // barrier, while this item's epilogue runs.
     prefetched = next_ntiles > 0 && ntiles > 0;
-    if (prefetched) load_q(slot * BR + wave * 32 + l32);
     b0 = (b0 + ntiles) & 1;
+    if (prefetched) load_q(slot * BR, b0 ^ 1);
 
     // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l) ----
     const float l_tot = xhalf_sum(l_run);
