@@ -171,8 +171,17 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
             fetch_vec(qt0);
             store_vec(0);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K, V registers and the first stage
-        tile_barrier();
+    }
+    // vmcnt(0): K, V registers and the first stage.  The compiler is then
+    // told the registers are loaded (mark_loaded), so it puts no waits for
+    // them inside the walk, where the hardware counter also counts the next
+    // stage's copies.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (qt0 < n_qt) tile_barrier();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        mark_loaded(kreg[kk]);
+        mark_loaded(vreg[kk]);
     }
 
     for (int qt = qt0; qt < n_qt; ++qt) {
@@ -247,6 +256,10 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
             if (wave == 0) store_vec(st ^ 1);
             vmem_wait_all();   // this wave's copies of the next stage landed
         }
+        // the next step's LSE2 / D loads are complete on every path (see
+        // mark_loaded), so the next fetch_vec adds no wait behind the copies
+        mark_loaded(nl2);
+        mark_loaded(ndd);
         tile_barrier();
     }
 
@@ -340,11 +353,18 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dqacc[db] = zero16();
 
-    if (ntiles > 0) {
-        load_tile(0, 0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q, dO registers and the first tiles
-        tile_barrier();
+    if (ntiles > 0) load_tile(0, 0);
+    // vmcnt(0): Q, dO, LSE2, D registers and the first tiles; then the same
+    // mark_loaded as in the dK/dV kernel
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (ntiles > 0) tile_barrier();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        mark_loaded(qreg[kk]);
+        mark_loaded(doreg[kk]);
     }
+    mark_loaded(l2);
+    mark_loaded(dd);
 
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * BC;

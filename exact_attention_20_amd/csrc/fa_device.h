@@ -152,6 +152,18 @@ __device__ __forceinline__ void async_load_lds16(i32x4 rsrc, uint32_t lds_addr, 
 
 __device__ __forceinline__ void vmem_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// An empty statement that reads `x`.  The compiler's wait analysis does not
+// treat an explicit s_waitcnt as completing the loads it tracks, but it does
+// place its own wait before an instruction that reads their results and then
+// regards them as complete.  Reading every register loaded before a tile
+// loop, at a point where the hardware has already waited for them (after the
+// prologue's vmcnt(0)), keeps it from putting waits inside the loop, where
+// the hardware counter also counts the asynchronous copies of the next tile.
+template <typename T>
+__device__ __forceinline__ void mark_loaded(const T& x) {
+    asm volatile("" ::"v"(x));
+}
+
 // Workgroup barrier between LDS phases of the tile loops.  The scheduling
 // barriers keep every instruction on its side of it, whatever the machine
 // scheduler's alias reasoning about the asynchronous copies (which it cannot
