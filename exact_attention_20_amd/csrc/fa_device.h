@@ -294,18 +294,32 @@ struct TileCopy {
     }
 };
 
-// Workgroup id -> (batch*head, tile index).  Consecutive workgroup ids go to
-// the 8 XCDs round robin, so ids are regrouped to give each XCD a contiguous
-// run of heads (their K/V, or Q/dO, then share that XCD's L2).  Tiles of a
-// head come out in ascending order.
+// Workgroup id -> (batch*head, tile index), for total = (batch*head count) x
+// n_tiles workgroups.  Consecutive workgroup ids go to the 8 XCDs round
+// robin, so ids are regrouped to give each XCD a contiguous run of heads
+// (their K/V, or Q/dO, then share that XCD's L2).  Within the run, the tiles
+// of two consecutive heads alternate: 0 of head 2g, 0 of head 2g+1, 1 of 2g,
+// ...  Callers issue the heaviest causal tile first, so the heavy tiles of
+// both heads start before the light ones of either; the light tiles then
+// fill the slots that free up at the end instead of one head's last heavy
+// tiles running alone (a greedy-dispatch model of one XCD gives a tail of
+// 10% of the run with one head at a time, none with two).  An odd last head
+// keeps its own order.
 __device__ __forceinline__ void map_head_tile(int w, int total, int n_tiles, int& bh, int& tile) {
     int L = w;
     if ((total & 7) == 0) {
         const int per = total >> 3;
         L = (w & 7) * per + (w >> 3);
     }
-    bh = L / n_tiles;
-    tile = L - bh * n_tiles;
+    const int n_heads = total / n_tiles;
+    const int g = L / (2 * n_tiles), r = L - g * 2 * n_tiles;
+    if (2 * g + 1 < n_heads) {
+        bh = 2 * g + (r & 1);
+        tile = r >> 1;
+    } else {
+        bh = 2 * g;
+        tile = r;
+    }
 }
 
 }  // namespace fa
