@@ -57,8 +57,14 @@ constexpr float kRescaleSlack = 8.0f;
 // query tile, run); each writes its normalised partial O (fp32) and partial
 // LSE (log2 units) to p.o_part / p.lse_part, and fwd_combine_kernel merges
 // them.  Without SPLIT the workgroup owns whole query tiles.
+// Waves per SIMD the register budget must allow: 2 at d = 128 (LDS holds
+// two workgroups per CU), 4 at d = 64 (32 KiB of LDS per workgroup, so four
+// workgroups per CU fit if the kernel stays within 128 VGPRs).
+template <int D>
+constexpr int fwd_waves_per_simd() { return D == 64 ? 4 : 2; }
+
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
+__global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(FwdParams p) {
     constexpr int BR = 128, BC = 64;
     constexpr int NKK = D / 16;        // k-steps over d for S^T
     constexpr int NKB = BC / 32;       // 32-key blocks per tile
@@ -278,11 +284,13 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
     }
 
     // The next item's first key tile is already in LDS (buffer b0 below);
-    // its Q tile is copied into the other buffer, idle since the loop's last
-    // barrier, while this item's epilogue runs.
+    // the other buffer is idle since the loop's last barrier.  At d = 128 the
+    // epilogue stages O there first; otherwise it takes the next item's Q
+    // tile right away, while this item's epilogue runs.
     prefetched = next_ntiles > 0 && ntiles > 0;
     b0 = (b0 + ntiles) & 1;
-    if (prefetched) load_q(slot * BR, b0 ^ 1);
+    constexpr bool kStageO = D == 128;
+    if (!kStageO && prefetched) load_q(slot * BR, b0 ^ 1);
 
     // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l) ----
     const float l_tot = xhalf_sum(l_run);
@@ -306,7 +314,35 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
         }
         continue;
     }
-    if (qi < Nq) {
+    // At d = 128, O goes through LDS so that HBM sees whole rows: a lane
+    // holds one query's d values in 8-byte pieces, so direct stores write 32
+    // scattered 16-byte pieces per instruction and stall on their data
+    // registers.  Each wave writes its 32 rows into its own part of the idle
+    // buffer (swizzled like the K/V tiles), reads them back row-contiguous
+    // and stores 16 bytes per lane; no other wave touches those rows.  (At
+    // d = 64 the staging costs more than it saves: its registers push the
+    // kernel past the 128 VGPRs of four waves per SIMD.)
+    if constexpr (kStageO) {
+        char* ost = smem + (b0 ^ 1) * BUF_BYTES + wave * 32 * (D * 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+                w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                *(u32x2*)(ost + tile_offset<D>(l32, db * 4 + g) + hg * 8) = w;
+            }
+        constexpr int CPR = D / 8;          // 16-byte chunks per row
+        constexpr int RPI = 64 / CPR;       // rows per 64-lane pass
+        bf16* Ow = (bf16*)p.o + (size_t)bh * Nq * D + (size_t)qw * D;
+#pragma unroll
+        for (int r0 = 0; r0 < 32; r0 += RPI) {
+            const int r = r0 + lane / CPR, c = lane % CPR;
+            const u32x4 x = *(const u32x4*)(ost + tile_offset<D>(r, c));
+            if (qw + r < Nq) *(u32x4*)(Ow + (size_t)r * D + c * 8) = x;
+        }
+    } else if (qi < Nq) {
         bf16* Oh = (bf16*)p.o + (size_t)bh * Nq * D + (size_t)qi * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -317,8 +353,14 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdParams p) {
                 w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
                 *(u32x2*)(Oh + db * 32 + g * 8 + 4 * hg) = w;
             }
-        if (hg == 0 && p.lse)
-            p.lse[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    if (qi < Nq && hg == 0 && p.lse)
+        p.lse[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (kStageO && more) {
+        // every wave has read its staged rows before the buffer takes the
+        // next item's Q tile (or, unprefetched, that item's own copies)
+        tile_barrier();
+        if (prefetched) load_q(slot * BR, b0 ^ 1);
     }
     }   // items
 }
