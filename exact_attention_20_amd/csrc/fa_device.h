@@ -150,6 +150,58 @@ __device__ __forceinline__ void async_load_lds16(i32x4 rsrc, uint32_t lds_addr, 
         : "memory");
 }
 
+// Eight such copies in one statement: 1 KiB each to consecutive LDS
+// addresses lds_addr, lds_addr + 1024, ... from per-lane offsets off[i] +
+// soff.  M0 is bound as an input (the compiler writes it); the statement
+// steps it by 1 KiB per copy and steps it back at the end, so M0 leaves the
+// statement holding the value the compiler put there.  The wait states are
+// paid once up front (5: VALU write of an SGPR operand before the
+// statement), then 1 after each M0 step.
+__device__ __forceinline__ void async_load_lds16_x8(i32x4 rsrc, uint32_t lds_addr, const uint32_t (&off)[8],
+                                                    uint32_t soff) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 %0, %8, %9 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %8, %9 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %8, %9 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %3, %8, %9 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %4, %8, %9 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %5, %8, %9 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %6, %8, %9 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %7, %8, %9 offen lds\n\t"
+        "s_sub_u32 m0, m0, 0x1c00"
+        :
+        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "v"(off[5]), "v"(off[6]),
+          "v"(off[7]), "s"(rsrc), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory", "scc");
+}
+
+// The same for four copies.
+__device__ __forceinline__ void async_load_lds16_x4(i32x4 rsrc, uint32_t lds_addr, const uint32_t (&off)[4],
+                                                    uint32_t soff) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 %0, %4, %5 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %4, %5 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %4, %5 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %3, %4, %5 offen lds\n\t"
+        "s_sub_u32 m0, m0, 0xc00"
+        :
+        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(rsrc), "s"(soff),
+          "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory", "scc");
+}
+
 __device__ __forceinline__ void vmem_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // An empty statement that reads `x`.  The compiler's wait analysis does not
@@ -289,8 +341,14 @@ struct TileCopy {
     // device), so rows past the end still read as zero.
     __device__ __forceinline__ void issue(const i32x4& rsrc, int row0, uint32_t dst) const {
         const uint32_t soff = (uint32_t)row0 * D * 2;
+        if constexpr (LOADS == 8) {
+            async_load_lds16_x8(rsrc, dst + lds_off, goff, soff);
+        } else if constexpr (LOADS == 4) {
+            async_load_lds16_x4(rsrc, dst + lds_off, goff, soff);
+        } else {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) async_load_lds16(rsrc, dst + lds_off + i * 1024, goff[i], soff);
+            for (int i = 0; i < LOADS; ++i) async_load_lds16(rsrc, dst + lds_off + i * 1024, goff[i], soff);
+        }
     }
 };
 
