@@ -21,6 +21,7 @@ or a library routine.  No function here is "parity unpinned".
 
 from .attention import (  # noqa: F401
     visible_mask,
+    window_bounds,
     attention_forward,
     attention_forward_rows,
     attention_backward,

@@ -22,6 +22,11 @@ Readings taken where the pages are silent or disagree:
   * LSE = m + ln(l) uses the natural logarithm ([P2] §3, [P5] FA2 step 4);
   * causal masking is bottom-right aligned: key j is visible to query i iff
     j <= i + (Nk - Nq) (the pages never fix it; for Nq == Nk it is j <= i);
+  * a local window (wl, wr) keeps key j for query i iff
+    i + off - wl <= j <= i + off + wr with off = Nk - Nq, either side
+    unbounded when None: the pages define no window; this is the plainest
+    extension of the causal rule (causal is (None, 0), a sliding window of W
+    keys is (W - 1, 0));
   * a query row with no visible key has O = 0 and LSE = -inf, and contributes
     nothing to the gradients.
 """
@@ -36,18 +41,38 @@ NEG_INF = -np.inf
 # ----------------------------------------------------------------------------
 # masking
 # ----------------------------------------------------------------------------
-def visible_mask(Nq: int, Nk: int, causal: bool, rows=None) -> np.ndarray:
+def window_bounds(causal: bool, window):
+    """(wl, wr) of the mask: ``window`` itself when given (then ``causal``
+    must be False), else (None, 0) for causal and (None, None) otherwise."""
+    if window is None:
+        return (None, 0) if causal else (None, None)
+    if causal:
+        raise ValueError("give either causal or a window, not both")
+    wl, wr = window
+    for w in (wl, wr):
+        if w is not None and w < 0:
+            raise ValueError("window sides are None (unbounded) or >= 0")
+    return wl, wr
+
+
+def visible_mask(Nq: int, Nk: int, causal: bool, rows=None, window=None) -> np.ndarray:
     """Boolean [len(rows), Nk]: True where key j is visible to query i.
 
     Non-causal: every key is visible.  Causal ([P2] §3 'apply_mask'): key j is
     visible to query i iff j <= i + (Nk - Nq) (bottom-right alignment, the
-    reading taken here; it is j <= i when Nq == Nk).
+    reading taken here; it is j <= i when Nq == Nk).  Window (wl, wr): iff
+    i + off - wl <= j <= i + off + wr, off = Nk - Nq, a None side unbounded.
     """
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
-    if not causal:
-        return np.ones((rows.size, Nk), dtype=bool)
+    wl, wr = window_bounds(causal, window)
     j = np.arange(Nk)[None, :]
-    return j <= (rows[:, None] + (Nk - Nq))
+    diag = rows[:, None] + (Nk - Nq)
+    ok = np.ones((rows.size, Nk), dtype=bool)
+    if wr is not None:
+        ok &= j <= diag + wr
+    if wl is not None:
+        ok &= j >= diag - wl
+    return ok
 
 
 # ----------------------------------------------------------------------------
@@ -66,7 +91,7 @@ def softmax(x) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # the definition: materialise S and P (one head)
 # ----------------------------------------------------------------------------
-def _head_forward(q, k, v, scale, causal, rows):
+def _head_forward(q, k, v, scale, causal, rows, window=None):
     """One head.  q [r, d] holds the query rows ``rows`` of a sequence of
     length Nq; k [Nk, d]; v [Nk, dv].  Returns (O [r, dv], LSE [r], P [r, Nk]).
 
@@ -77,7 +102,7 @@ def _head_forward(q, k, v, scale, causal, rows):
     Nq, Nk = rows[1], k.shape[0]
     idx = rows[0]
     S = scale * (q @ k.T)
-    S = np.where(visible_mask(Nq, Nk, causal, idx), S, NEG_INF)
+    S = np.where(visible_mask(Nq, Nk, causal, idx, window), S, NEG_INF)
     m = np.max(S, axis=1) if Nk > 0 else np.full(q.shape[0], NEG_INF)
     empty = ~np.isfinite(m)
     m_safe = np.where(empty, 0.0, m)
@@ -96,7 +121,7 @@ def _as_f64(*arrs):
     return [np.asarray(a, dtype=np.float64) for a in arrs]
 
 
-def attention_forward(q, k, v, scale: float, causal: bool):
+def attention_forward(q, k, v, scale: float, causal: bool, window=None):
     """O and LSE for q [..., Nq, d], k [..., Nk, d], v [..., Nk, dv].
 
     Leading dimensions (batch, head) are independent ([P1] §4.1: attention is
@@ -110,11 +135,11 @@ def attention_forward(q, k, v, scale: float, causal: bool):
     L = np.empty(lead + (Nq,))
     for ix in np.ndindex(*lead):
         O[ix], L[ix], _ = _head_forward(q[ix], k[ix], v[ix], scale, causal,
-                                        (np.arange(Nq), Nq))
+                                        (np.arange(Nq), Nq), window)
     return O, L
 
 
-def attention_forward_rows(q, k, v, scale: float, causal: bool, rows):
+def attention_forward_rows(q, k, v, scale: float, causal: bool, rows, window=None):
     """Like ``attention_forward`` but only for the query indices ``rows``
     (the same rows for every head).  q is the full [..., Nq, d] tensor; the
     result holds O [..., len(rows), dv] and LSE [..., len(rows)].  Used where
@@ -126,11 +151,11 @@ def attention_forward_rows(q, k, v, scale: float, causal: bool, rows):
     L = np.empty(lead + (rows.size,))
     for ix in np.ndindex(*lead):
         qh, kh, vh = _as_f64(q[ix][rows], k[ix], v[ix])
-        O[ix], L[ix], _ = _head_forward(qh, kh, vh, scale, causal, (rows, Nq))
+        O[ix], L[ix], _ = _head_forward(qh, kh, vh, scale, causal, (rows, Nq), window)
     return O, L
 
 
-def attention_backward(q, k, v, do, scale: float, causal: bool):
+def attention_backward(q, k, v, do, scale: float, causal: bool, window=None):
     """Gradients of sum(dO * O) w.r.t. Q, K, V, by [P2] §5:
         dV = P^T dO;  dP = dO V^T;  D = rowsum(dO * O);
         dS = P * (dP - D);  dQ = scale * dS K;  dK = scale * dS^T Q.
@@ -148,7 +173,7 @@ def attention_backward(q, k, v, do, scale: float, causal: bool):
     D = np.empty(lead + (Nq,))
     for ix in np.ndindex(*lead):
         Oh, Lh, P = _head_forward(q[ix], k[ix], v[ix], scale, causal,
-                                  (np.arange(Nq), Nq))
+                                  (np.arange(Nq), Nq), window)
         dOh = do[ix]
         dvv[ix] = P.T @ dOh
         dP = dOh @ v[ix].T
@@ -174,7 +199,7 @@ def online_rescale(m, l, block_max, block_sum_at_new_max=0.0):
 
 
 def tiled_forward(q, k, v, scale: float, causal: bool, block_q: int,
-                  block_k: int, trace: bool = False):
+                  block_k: int, trace: bool = False, window=None):
     """FA2 forward recurrence with deferred normalisation ([P2] §3; [P5]
     FlashAttention-2 algorithm), for one head: q [Nq, d], k [Nk, d], v [Nk, dv].
 
@@ -203,7 +228,7 @@ def tiled_forward(q, k, v, scale: float, causal: bool, block_q: int,
         for j0 in range(0, Nk, block_k):
             cols = slice(j0, min(j0 + block_k, Nk))
             S = scale * (Qi @ k[cols].T)
-            vis = visible_mask(Nq, Nk, causal, rows)[:, cols]
+            vis = visible_mask(Nq, Nk, causal, rows, window)[:, cols]
             S = np.where(vis, S, NEG_INF)
             m_new = np.maximum(m, np.max(S, axis=1))
             live = np.isfinite(m_new)
@@ -226,7 +251,7 @@ def tiled_forward(q, k, v, scale: float, causal: bool, block_q: int,
 
 
 def tiled_forward_renormalised(q, k, v, scale: float, causal: bool,
-                               block_q: int, block_k: int):
+                               block_q: int, block_k: int, window=None):
     """Tiled forward that keeps the accumulator *normalised* after every key
     block ([P1] §4.6 with eq. (9); [P3] Step 1 update formulas):
         l_new = l * exp(m - m_new) + rowsum exp(S - m_new)
@@ -246,7 +271,7 @@ def tiled_forward_renormalised(q, k, v, scale: float, causal: bool,
         for j0 in range(0, Nk, block_k):
             cols = slice(j0, min(j0 + block_k, Nk))
             S = scale * (Qi @ k[cols].T)
-            S = np.where(visible_mask(Nq, Nk, causal, rows)[:, cols], S, NEG_INF)
+            S = np.where(visible_mask(Nq, Nk, causal, rows, window)[:, cols], S, NEG_INF)
             m_new = np.maximum(m, np.max(S, axis=1))
             live = np.isfinite(m_new)
             base = np.where(live, m_new, 0.0)
@@ -262,14 +287,16 @@ def tiled_forward_renormalised(q, k, v, scale: float, causal: bool,
     return O, L
 
 
-def attention_flops(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool) -> int:
+def attention_flops(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool,
+                    window=None) -> int:
     """Forward FLOPs counted over visible (query, key) pairs only: two
     products of 2*d FLOPs per pair ([P2] §1: the work sits in the two
-    matrix products).  Counts pairs with ``visible_mask``'s rule."""
-    if not causal:
-        pairs = Nq * Nk
-    else:
-        off = Nk - Nq
-        i = np.arange(Nq, dtype=np.int64)
-        pairs = int(np.sum(np.clip(i + off + 1, 0, Nk)))
+    matrix products).  Counts pairs with ``visible_mask``'s rule: query i
+    sees the keys [i + off - wl, i + off + wr] clipped to [0, Nk)."""
+    wl, wr = window_bounds(causal, window)
+    off = Nk - Nq
+    i = np.arange(Nq, dtype=np.int64)
+    hi = np.full(Nq, Nk, dtype=np.int64) if wr is None else np.clip(i + off + wr + 1, 0, Nk)
+    lo = np.zeros(Nq, dtype=np.int64) if wl is None else np.clip(i + off - wl, 0, Nk)
+    pairs = int(np.sum(np.maximum(hi - lo, 0)))
     return 4 * d * pairs * B * H

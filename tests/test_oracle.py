@@ -355,3 +355,164 @@ def test_flop_count_matches_mask():
     for (Nq, Nk, causal) in [(64, 64, True), (30, 70, True), (70, 30, True), (33, 65, False)]:
         pairs = int(visible_mask(Nq, Nk, causal).sum())
         assert oracle.attention_flops(2, 3, Nq, Nk, 16, causal) == 4 * 16 * pairs * 6
+
+
+# ------------------------------------------------------ local window (f4)
+# Windows (wl, wr): key j visible to query i iff i+off-wl <= j <= i+off+wr,
+# off = Nk - Nq, None = unbounded (the reading documented in oracle.attention).
+WINDOWS = [(3, 0), (0, 0), (5, 2), (None, 1), (2, None), (40, 0), (0, 7)]
+
+
+def _brute_window_row(qi, K, V, scale, lo, hi):
+    """One row by explicit enumeration of the visible keys, math.exp only."""
+    keys = [j for j in range(K.shape[0]) if lo <= j <= hi]
+    if not keys:
+        return np.zeros(V.shape[1]), -math.inf
+    s = [scale * float(np.dot(qi, K[j])) for j in keys]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    tot = sum(w)
+    out = sum(wj * V[j] for wj, j in zip(w, keys)) / tot
+    return out, m + math.log(tot)
+
+
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("Nq,Nk", [(9, 9), (5, 11), (11, 5)])
+def test_window_forward_brute_force(window, Nq, Nk):
+    r = rng(20)
+    d = 3
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, 2))
+    O, L = attention_forward(q, k, v, 0.8, False, window=window)
+    wl, wr = window
+    off = Nk - Nq
+    for i in range(Nq):
+        lo = -10**9 if wl is None else i + off - wl
+        hi = 10**9 if wr is None else i + off + wr
+        o_ref, l_ref = _brute_window_row(q[i], k, v, 0.8, lo, hi)
+        assert np.max(np.abs(O[i] - o_ref)) <= 1e-12
+        assert (L[i] == l_ref == -math.inf) or abs(L[i] - l_ref) <= 1e-12
+
+
+@pytest.mark.parametrize("window", [(4, 0), (2, 3), (7, 1)])
+def test_window_equals_unmasked_attention_on_the_slice(window):
+    # each row's result is the plain (unmasked) definition over its key slice
+    r = rng(21)
+    Nq, Nk, d = 13, 17, 4
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    O, L = attention_forward(q, k, v, 0.5, False, window=window)
+    wl, wr = window
+    off = Nk - Nq
+    for i in range(Nq):
+        lo, hi = max(0, i + off - wl), min(Nk - 1, i + off + wr)
+        Os, Ls = attention_forward(q[i:i + 1], k[lo:hi + 1], v[lo:hi + 1], 0.5, False)
+        assert np.max(np.abs(O[i] - Os[0])) <= 1e-13
+        assert abs(L[i] - Ls[0]) <= 1e-13
+
+
+def test_window_closed_forms_and_limits():
+    r = rng(22)
+    Nq, Nk, d = 6, 9, 5
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    off = Nk - Nq
+    # a window of one key: O_i = V_{i+off}, LSE_i = scale * q_i . k_{i+off}
+    O, L = attention_forward(q, k, v, 0.7, False, window=(0, 0))
+    for i in range(Nq):
+        assert np.max(np.abs(O[i] - v[i + off])) <= 1e-14
+        assert abs(L[i] - 0.7 * float(q[i] @ k[i + off])) <= 1e-14
+    # unbounded left with right bound 0 is causal; bounds past the sequence change nothing
+    Oc, Lc = attention_forward(q, k, v, 0.7, True)
+    Ow, Lw = attention_forward(q, k, v, 0.7, False, window=(Nk + Nq, 0))
+    assert np.array_equal(Oc, Ow) and np.array_equal(Lc, Lw)
+    On, Ln = attention_forward(q, k, v, 0.7, False)
+    Ow, Lw = attention_forward(q, k, v, 0.7, False, window=(Nk + Nq, Nk + Nq))
+    assert np.array_equal(On, Ow) and np.array_equal(Ln, Lw)
+    # rows whose window lies wholly outside the keys are empty
+    O, L = attention_forward(q, k[:2], v[:2], 0.7, False, window=(1, 0))
+    off2 = 2 - Nq
+    for i in range(Nq):
+        if i + off2 + 0 < 0 or i + off2 - 1 > 1:
+            assert np.all(O[i] == 0.0) and L[i] == -math.inf
+    with pytest.raises(ValueError):
+        attention_forward(q, k, v, 0.7, True, window=(1, 0))
+    with pytest.raises(ValueError):
+        attention_forward(q, k, v, 0.7, False, window=(-1, 0))
+
+
+def test_window_keys_outside_do_not_matter_bitwise():
+    r = rng(23)
+    Nq, Nk, d = 16, 16, 4
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    O, L = attention_forward(q, k, v, 0.9, False, window=(3, 1))
+    k2, v2 = k.copy(), v.copy()
+    i = 10            # row 10 sees keys 7..11
+    for j in list(range(0, 7)) + list(range(12, Nk)):
+        k2[j] += 100.0
+        v2[j] -= 7.0
+    O2, L2 = attention_forward(q, k2, v2, 0.9, False, window=(3, 1))
+    assert np.array_equal(O[i], O2[i]) and L[i] == L2[i]
+
+
+@pytest.mark.parametrize("window", [(2, 0), (1, 2), (None, 1)])
+def test_window_backward_finite_differences(window):
+    r = rng(24)
+    Nq, Nk, d, dv = 6, 7, 3, 2
+    q, k = r.standard_normal((Nq, d)), r.standard_normal((Nk, d))
+    v, do = r.standard_normal((Nk, dv)), r.standard_normal((Nq, dv))
+    scale = 0.6
+    dq, dk, dvv, *_ = attention_backward(q, k, v, do, scale, False, window=window)
+
+    def loss():
+        O, _ = attention_forward(q, k, v, scale, False, window=window)
+        return float(np.sum(O * do))
+
+    h = 1e-6
+    for X, G in ((q, dq), (k, dk), (v, dvv)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(*X.shape):
+            old = X[idx]
+            X[idx] = old + h
+            fp = loss()
+            X[idx] = old - h
+            fm = loss()
+            X[idx] = old
+            num[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(num - G)) <= 1e-7 * max(1.0, np.max(np.abs(G)))
+
+
+def test_window_backward_matches_torch_autograd_fp64():
+    r = rng(25)
+    N, d, wl, wr = 29, 6, 5, 2
+    q, k, v, do = (r.standard_normal((1, 2, N, d)) for _ in range(4))
+    scale = 1 / math.sqrt(d)
+    dq, dk, dvv, O, L, D = attention_backward(q, k, v, do, scale, False, window=(wl, wr))
+    hide = torch.ones(N, N, dtype=torch.bool)   # True = masked, built row by row
+    for i in range(N):
+        for j in range(max(0, i - wl), min(N, i + wr + 1)):
+            hide[i, j] = False
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    s = ((tq @ tk.transpose(-1, -2)) * scale).masked_fill(hide, float("-inf"))
+    out = torch.softmax(s, dim=-1) @ tv
+    out.backward(torch.from_numpy(do))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dvv, tv.grad)):
+        assert np.max(np.abs(mine - ref.numpy())) <= 1e-12
+    assert np.max(np.abs(L - torch.logsumexp(s, dim=-1).detach().numpy())) <= 1e-12
+
+
+@pytest.mark.parametrize("bq,bk", [(4, 3), (64, 64), (5, 16)])
+def test_window_tiled_equals_untiled(bq, bk):
+    r = rng(26)
+    Nq, Nk, d = 37, 45, 8
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    for window in [(6, 0), (3, 4), (None, 2)]:
+        O, L = attention_forward(q, k, v, 0.4, False, window=window)
+        Ot, Lt = tiled_forward(q, k, v, 0.4, False, bq, bk, window=window)
+        Or, Lr = tiled_forward_renormalised(q, k, v, 0.4, False, bq, bk, window=window)
+        assert np.max(np.abs(Ot - O)) <= 1e-12 and np.max(np.abs(Or - O)) <= 1e-12
+        fin = np.isfinite(L)
+        assert np.array_equal(fin, np.isfinite(Lt)) and np.max(np.abs(Lt[fin] - L[fin])) <= 1e-12
+
+
+def test_window_flop_count_matches_mask():
+    for (Nq, Nk, window) in [(64, 64, (15, 0)), (30, 70, (3, 5)), (70, 30, (None, 2)), (33, 33, (4, None))]:
+        pairs = int(visible_mask(Nq, Nk, False, window=window).sum())
+        assert oracle.attention_flops(2, 3, Nq, Nk, 16, False, window=window) == 4 * 16 * pairs * 6
