@@ -40,20 +40,25 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["exact_attention_20_amd/csrc/fa_fwd.hip", "exact_attention_20_amd/csrc/fa_device.h"]
 
 
-def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
+def visible_pairs(Nq: int, Nk: int, causal: bool, window=None) -> int:
     """Number of (query, key) pairs the mask leaves visible (bottom-right
-    aligned causal mask: key j visible to query i iff j <= i + Nk - Nq)."""
-    if not causal:
+    aligned causal mask: key j visible to query i iff j <= i + Nk - Nq; a
+    local window (wl, wr): iff i + off - wl <= j <= i + off + wr, off = Nk - Nq,
+    a None side unbounded)."""
+    if window is None and not causal:
         return Nq * Nk
+    wl, wr = window if window is not None else (None, 0)
     off = Nk - Nq
     total = 0
     for i in range(Nq):
-        total += min(Nk, max(0, i + off + 1))
+        lo = 0 if wl is None else max(0, i + off - wl)
+        hi = Nk - 1 if wr is None else min(Nk - 1, i + off + wr)
+        total += max(0, hi - lo + 1)
     return total
 
 
 def fwd_flops(w) -> int:
-    return 4 * w.d * visible_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
+    return 4 * w.d * visible_pairs(w.Nq, w.Nk, w.causal, w.window) * w.B * w.H
 
 
 def algorithmic_bytes(w) -> int:
@@ -103,7 +108,7 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
         b, h = divmod(done, w.H)
         qh, kh, vh = (t[b, h].double().numpy() for t in (q, k, v))
         t0 = time.perf_counter()
-        attention_forward(qh, kh, vh, w.scale, w.causal)
+        attention_forward(qh, kh, vh, w.scale, w.causal, window=w.window)
         t_total += time.perf_counter() - t0
         done += 1
     rate = per_head_flops * done / t_total / 1e12
@@ -127,10 +132,12 @@ def time_launches(fn, stream, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
-def train_step_timing(fa, wl, steps: int, warmup: int):
+def train_step_timing(fa, wl, steps: int, warmup: int, window=None):
     """fa_fwd then fa_bwd on the training-step workload (B=4 H=16 N=4096
     d=64 bf16 causal), each timed on its own with HIP events; inputs, outputs
-    and the backward workspace are resident before timing starts."""
+    and the backward workspace are resident before timing starts.  With a
+    local ``window`` (wl, wr) the same shape runs fa_fwd_window and
+    fa_bwd_window instead of the causal calls."""
     import torch
     w = wl.TRAIN_STEP
     dev = torch.device("cuda:0")
@@ -149,25 +156,35 @@ def train_step_timing(fa, wl, steps: int, warmup: int):
                 w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), fa.FA_BF16,
                 ws.data_ptr(), need, sh)
 
+    f_fwd, f_bwd = fa.fa_fwd, fa.fa_bwd
+    if window is not None:
+        wa = tuple(-1 if x is None else x for x in window)
+        fwd_args = fwd_args[:11] + wa + fwd_args[12:]
+        bwd_args = bwd_args[:15] + wa + bwd_args[16:]
+        f_fwd, f_bwd = fa.fa_fwd_window, fa.fa_bwd_window
+
     def fwd():
-        st = fa.fa_fwd(*fwd_args)
+        st = f_fwd(*fwd_args)
         if st != 0:
-            raise fa.FAError(st, "fa_fwd")
+            raise fa.FAError(st, f_fwd.__name__)
 
     def bwd():
-        st = fa.fa_bwd(*bwd_args)
+        st = f_bwd(*bwd_args)
         if st != 0:
-            raise fa.FAError(st, "fa_bwd")
+            raise fa.FAError(st, f_bwd.__name__)
 
     fwd()
     ms_f = time_launches(fwd, stream, steps, warmup)
     ms_b = time_launches(bwd, stream, steps, warmup)
-    pairs = visible_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
-    return {"workload": w.name, "shape": w.describe(),
+    causal = w.causal if window is None else False
+    pairs = visible_pairs(w.Nq, w.Nk, causal, window) * w.B * w.H
+    shape = w.describe() if window is None else w.describe().replace("causal", f"window {window}")
+    return {"workload": w.name, "shape": shape,
             "fwd_ms": round(ms_f, 5), "fwd_tflops": round(4 * w.d * pairs / ms_f / 1e9, 3),
             "bwd_ms": round(ms_b, 5), "bwd_tflops": round(10 * w.d * pairs / ms_b / 1e9, 3),
             "bwd_flops": 10 * w.d * pairs,
-            "note": "bwd = D pre-pass + main kernel + dq convert; 10*d FLOPs per visible pair"}
+            "note": "bwd = prep (D, LSE*log2e) + dK/dV kernel + dQ kernel; 10*d FLOPs per "
+                    "visible pair"}
 
 
 def _counter_means(csv_dir: str, counter: str):
@@ -284,6 +301,15 @@ def main():
         if st != 0:
             raise fa.FAError(st, "fa_fwd")
 
+    if w.window is not None:
+        # local window: fa_fwd_window, (wl, wr) in place of the causal flag
+        wargv = argv[:11] + tuple(-1 if x is None else x for x in w.window) + argv[12:]
+
+        def step():  # noqa: F811
+            st = fa.fa_fwd_window(*wargv)
+            if st != 0:
+                raise fa.FAError(st, "fa_fwd_window")
+
     # Decoding (a few query rows against a long key range) runs the split-KV
     # path: it is HBM-bound, so its roofline is the 8 TB/s HBM peak.
     decode = w.name == "decode_bf16"
@@ -316,6 +342,11 @@ def main():
 
     traffic = traffic_for(w.name)
     nbytes = algorithmic_bytes(w)
+    if w.window is not None:
+        wl_, wr_ = w.window
+        result_window = {"window": [wl_, wr_]}
+    else:
+        result_window = {}
     result = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -330,7 +361,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1) inputs of the workload's shape)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "lse_saved": True, "flops_per_step": flops},
+                   "causal": w.causal, **result_window, "lse_saved": True,
+                   "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
         "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -366,6 +398,9 @@ def main():
                           "note": "L2 and Infinity Cache flushed before each launch"}
     if not args.no_train_step:
         result["train_step"] = train_step_timing(fa, wl, steps=20, warmup=5)
+        if w.window is not None:
+            result["train_step_window"] = train_step_timing(fa, wl, steps=20, warmup=5,
+                                                            window=(1023, 0))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(result), flush=True)

@@ -13,14 +13,22 @@ Raw entry points, same names and argument order as ``include/fa.h``:
     fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal,
            dtype, workspace, workspace_bytes, stream) -> int
     fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) -> int
+    fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, d, scale, window_left, window_right,
+                  dtype, stream) -> int
+    fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, window_left,
+                  window_right, dtype, workspace, workspace_bytes, stream) -> int
     fa_strerror(status) -> str
 (pointer arguments are integers: device addresses, 0 for NULL)
 
 Tensor helpers that allocate the outputs with torch and raise ``FAError`` on a
 non-zero status:
-    attention_forward(q, k, v, scale=None, causal=False) -> (o, lse)
+    attention_forward(q, k, v, scale=None, causal=False, window=None) -> (o, lse)
     attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0) -> (o, lse)
-    attention_backward(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
+    attention_backward(q, k, v, o, lse, do, scale=None, causal=False, window=None)
+        -> (dq, dk, dv)
+``window`` is a local window (wl, wr): key j is visible to query i iff
+i + (Nk - Nq) - wl <= j <= i + (Nk - Nq) + wr, a side None for no bound; it
+replaces ``causal`` (giving both raises ValueError).
 """
 
 from __future__ import annotations
@@ -32,7 +40,7 @@ import os
 __all__ = [
     "FA_F32", "FA_BF16", "FAError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_strerror",
+    "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_bwd_window", "fa_strerror",
     "attention_forward", "attention_forward_splitkv", "attention_backward",
 ]
 
@@ -75,6 +83,11 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_fwd_window.restype = i
+    lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i,
+                                  vp, sz, vp]
+    lib.fa_bwd_window.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -112,6 +125,21 @@ def fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) -> int:
     return int(load_library().fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype))
 
 
+def fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, d, scale, window_left, window_right, dtype,
+                  stream) -> int:
+    return load_library().fa_fwd_window(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Nq, Nk, d,
+                                        float(scale), int(window_left), int(window_right),
+                                        int(dtype), _p(stream))
+
+
+def fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, window_left,
+                  window_right, dtype, workspace, workspace_bytes, stream) -> int:
+    return load_library().fa_bwd_window(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
+                                        _p(dk), _p(dv), B, H, Nq, Nk, d, float(scale),
+                                        int(window_left), int(window_right), int(dtype),
+                                        _p(workspace), int(workspace_bytes), _p(stream))
+
+
 def fa_strerror(status: int) -> str:
     return load_library().fa_strerror(int(status)).decode()
 
@@ -144,8 +172,21 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def attention_forward(q, k, v, scale=None, causal=False, out=None, lse=None, want_lse=True):
-    """O = softmax(scale * q k^T) v and the natural-log LSE, via fa_fwd.
+def _window_args(causal, window):
+    """(window_left, window_right) of the C ABI (-1 = unbounded), or None
+    when the call takes the causal flag."""
+    if window is None:
+        return None
+    if causal:
+        raise ValueError("give either causal or a window, not both")
+    wl, wr = window
+    return (-1 if wl is None else int(wl), -1 if wr is None else int(wr))
+
+
+def attention_forward(q, k, v, scale=None, causal=False, out=None, lse=None, want_lse=True,
+                      window=None):
+    """O = softmax(scale * q k^T) v and the natural-log LSE, via fa_fwd (or
+    fa_fwd_window when a local ``window`` is given).
 
     q [B,H,Nq,d], k and v [B,H,Nk,d]; bf16 or fp32; contiguous; on the GPU.
     Returns (o, lse); lse is None when want_lse is False and none is given.
@@ -165,11 +206,16 @@ def attention_forward(q, k, v, scale=None, causal=False, out=None, lse=None, wan
     if lse is not None:
         _check(lse, "lse", (B, H, Nq), torch.float32)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                lse.data_ptr() if lse is not None else 0, B, H, Nq, Nk, d, scale,
-                causal, _dtype_code(q), _stream())
+    w = _window_args(causal, window)
+    lse_p = lse.data_ptr() if lse is not None else 0
+    if w is None:
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
+                    B, H, Nq, Nk, d, scale, causal, _dtype_code(q), _stream())
+    else:
+        st = fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
+                           B, H, Nq, Nk, d, scale, w[0], w[1], _dtype_code(q), _stream())
     if st != 0:
-        raise FAError(st, "fa_fwd")
+        raise FAError(st, "fa_fwd" if w is None else "fa_fwd_window")
     return out, lse
 
 
@@ -200,9 +246,11 @@ def attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0, wor
     return out, lse
 
 
-def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
-    """dq, dk, dv of sum(do * o) via fa_bwd (bf16 only).  ``o`` and ``lse``
-    are the outputs of ``attention_forward`` for the same inputs."""
+def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=None,
+                       window=None):
+    """dq, dk, dv of sum(do * o) via fa_bwd, or fa_bwd_window (bf16 only).
+    ``o`` and ``lse`` are the outputs of ``attention_forward`` for the same
+    inputs and mask."""
     import torch
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
@@ -217,10 +265,15 @@ def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d,
-                scale, causal, code, workspace.data_ptr() if workspace is not None else 0,
-                workspace.numel() if workspace is not None else 0, _stream())
+    w = _window_args(causal, window)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    ws = (workspace.data_ptr() if workspace is not None else 0,
+          workspace.numel() if workspace is not None else 0)
+    if w is None:
+        st = fa_bwd(*ptrs, B, H, Nq, Nk, d, scale, causal, code, *ws, _stream())
+    else:
+        st = fa_bwd_window(*ptrs, B, H, Nq, Nk, d, scale, w[0], w[1], code, *ws, _stream())
     if st != 0:
-        raise FAError(st, "fa_bwd")
+        raise FAError(st, "fa_bwd" if w is None else "fa_bwd_window")
     return dq, dk, dv

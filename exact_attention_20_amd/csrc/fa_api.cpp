@@ -29,11 +29,34 @@ int check_common(int B, int H, int Nq, int Nk, int d, float scale, int dtype) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
-}  // namespace
+// Kernel mask of a call: a causal flag, or the reaches of a local window
+// (-1 = unbounded side).  A window unbounded on the left that reaches 0 keys
+// to the right is the causal mask and takes the causal kernels; one unbounded
+// on both sides takes the unmasked kernels.
+struct Mask {
+    int mode, wl, wr;
+};
 
-extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                      int dtype, void* stream) {
+Mask causal_mask(int causal) { return Mask{causal ? fa::kMaskCausal : fa::kMaskNone, 0, 0}; }
+
+int window_mask(int window_left, int window_right, Mask* m) {
+    if (window_left < -1 || window_right < -1) return FA_ERR_WINDOW;
+    if (window_left == -1 && window_right == -1) {
+        *m = Mask{fa::kMaskNone, 0, 0};
+    } else if (window_left == -1 && window_right == 0) {
+        *m = Mask{fa::kMaskCausal, 0, 0};
+    } else {
+        // reaches beyond any sequence are unbounded; clamping keeps the
+        // kernels' offset sums inside int
+        auto reach = [](int w) { return w < 0 || w > fa::kWindowUnbounded ? fa::kWindowUnbounded : w; };
+        *m = Mask{fa::kMaskWindow, reach(window_left), reach(window_right)};
+    }
+    return FA_OK;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Nq, int Nk, int d, float scale, Mask mask,
+             int dtype, void* stream) {
     int st = check_common(B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
     const long BH = (long)B * H;
@@ -53,14 +76,14 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
     p.Nq = Nq;
     p.Nk = Nk;
     p.n_qtiles = n_qtiles;
-    p.paired = fa::fwd_pair_tiles(dtype, d, causal != 0, BH, n_qtiles) ? 1 : 0;
+    p.paired = fa::fwd_pair_tiles(dtype, d, mask.mode == fa::kMaskCausal, BH, n_qtiles) ? 1 : 0;
     p.n_slots = p.paired ? (n_qtiles + 1) / 2 : n_qtiles;
     p.total_wg = (int)(BH * p.n_slots);
     p.scale_log2 = scale * 1.44269504088896340736f;
-    return hip_status(fa::launch_fwd(dtype, d, causal != 0, (int)BH, p, (hipStream_t)stream));
+    p.wl = mask.wl;
+    p.wr = mask.wr;
+    return hip_status(fa::launch_fwd(dtype, d, mask.mode, p, (hipStream_t)stream));
 }
-
-namespace {
 
 // Runs of 64-key tiles for the split-KV forward.  n_splits = 0 asks for
 // enough workgroups to cover the GPU's 512 resident slots four times (at
@@ -157,10 +180,12 @@ extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, in
     return 2 * vec;
 }
 
-extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                      const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dO, void* dq, void* dk, void* dv,
+             int B, int H, int Nq, int Nk, int d, float scale, Mask mask,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_common(B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
     if (dtype != FA_BF16) return FA_ERR_DTYPE;
@@ -193,13 +218,53 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
     p.Nk = Nk;
     p.BH = (int)BH;
     const int n_kt = (Nk + 127) / 128, n_qt = (Nq + 127) / 128;
-    p.kv_paired = fa::bwd_pair_tiles(causal != 0, BH, n_kt) ? 1 : 0;
+    const bool causal = mask.mode == fa::kMaskCausal;
+    p.kv_paired = fa::bwd_pair_tiles(causal, BH, n_kt) ? 1 : 0;
     p.kv_slots = p.kv_paired ? (n_kt + 1) / 2 : n_kt;
-    p.q_paired = fa::bwd_pair_tiles(causal != 0, BH, n_qt) ? 1 : 0;
+    p.q_paired = fa::bwd_pair_tiles(causal, BH, n_qt) ? 1 : 0;
     p.q_slots = p.q_paired ? (n_qt + 1) / 2 : n_qt;
     p.scale = scale;
     p.scale_log2 = scale * 1.44269504088896340736f;
-    return hip_status(fa::launch_bwd(d, causal != 0, p, (hipStream_t)stream));
+    p.wl = mask.wl;
+    p.wr = mask.wr;
+    return hip_status(fa::launch_bwd(d, mask.mode, p, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      int dtype, void* stream) {
+    return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal_mask(causal), dtype, stream);
+}
+
+extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Nq, int Nk, int d, float scale,
+                             int window_left, int window_right, int dtype, void* stream) {
+    Mask m;
+    const int st = window_mask(window_left, window_right, &m);
+    if (st != FA_OK) return st;
+    return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, d, scale, m, dtype, stream);
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal_mask(causal),
+                    dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                             int B, int H, int Nq, int Nk, int d, float scale,
+                             int window_left, int window_right, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    Mask m;
+    const int st = window_mask(window_left, window_right, &m);
+    if (st != FA_OK) return st;
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, m, dtype, workspace,
+                    workspace_bytes, stream);
 }
 
 extern "C" const char* fa_strerror(int status) {
@@ -213,6 +278,7 @@ extern "C" const char* fa_strerror(int status) {
         case FA_ERR_WORKSPACE: return "workspace is NULL or smaller than fa_bwd_workspace_bytes()";
         case FA_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
         case FA_ERR_SCALE: return "scale must be finite and > 0";
+        case FA_ERR_WINDOW: return "window reaches must be >= 0, or -1 for an unbounded side";
         default: return "unknown status";
     }
 }

@@ -77,7 +77,7 @@ __device__ __forceinline__ void pack_pairs(const float (&x)[16], u32x4& lo, u32x
 // values of LSE*log2e and D; two stages, the next one filled while the
 // current one is used.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParams p) {
     constexpr int BKV = 128, BQ = 64;
     constexpr int NQB = BQ / 32;              // 32-query blocks per step
@@ -92,6 +92,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hg = lane >> 5;
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+    // query q sees key j iff j <= q + offr (causal, windows) and, for a
+    // window, j >= q + offl (the mask family of the forward kernels)
+    constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
+    const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
+    const int offl = off - (MASK == kMaskWindow ? p.wl : 0);
     const int n_kt = (Nk + BKV - 1) / BKV;
     // key tiles of this workgroup: j (ascending j = heavy causal tiles
     // first), then with pairing its mirror n-1-j (equal causal work per
@@ -128,12 +133,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
         vreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rv, o, 0));
     }
 
-    // Query range: a query q sees key j iff j <= q + off (causal), so the
-    // walk starts at the first query tile that sees the tile's first key.
-    const int qstart = CAUSAL ? max(0, k0 - off) : 0;
+    // Query range: the walk starts at the first query tile that sees the
+    // tile's first key (q >= j - offr) and, for a window, ends after the last
+    // query that sees its last key (q <= j - offl).
+    const int qstart = kRight ? max(0, k0 - offr) : 0;
     const int qt0 = qstart / BQ;
-    const int n_qt = (Nq + BQ - 1) / BQ;
-    const int wq_first = CAUSAL ? kw - off : 0;   // first query that sees this wave's first key
+    const int qend = kLeft ? max(0, min(Nq, k0 + BKV - offl)) : Nq;
+    const int n_qt = (qend + BQ - 1) / BQ;
+    const int wq_first = kRight ? kw - offr : 0;        // first query that sees this wave's first key
+    const int wq_last = kLeft ? kw + 31 - offl : Nq;    // last query that sees its last key
 
     auto load_step = [&](int qt, int stage) {
         const uint32_t base = smem_lds + stage * STAGE;
@@ -197,7 +205,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
             if (wave == 0) fetch_vec(qt + 1);
         }
 
-        if (q0 + BQ - 1 >= wq_first) {
+        if (q0 + BQ - 1 >= wq_first && (!kLeft || q0 <= wq_last)) {
             // ---- S = Q K^T and dP = dO V^T (lane = key, items = queries) ----
             f32x16 s[NQB], dp[NQB];
 #pragma unroll
@@ -213,7 +221,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
                     dp[qb] = mfma_bf16(tile_read_row<D>(dos, qb * 32, kk, lane), vreg[kk], dp[qb]);
                 }
             // ---- P = 2^(S*scale*log2e - LSE2), dS = P * (dP - D) ----
-            const bool need_mask = (q0 + BQ > Nq) || (CAUSAL && q0 + off < kw + 31);
+            const bool need_mask = (q0 + BQ > Nq) || (kRight && q0 + offr < kw + 31) ||
+                                   (kLeft && q0 + BQ - 1 + offl > kw);
             u32x4 pw[NQC], dsw[NQC];
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
@@ -228,7 +237,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
                         float sv = s[qb][4 * g + e];
                         if (need_mask) {
                             const int q = q0 + ql + e;
-                            const bool vis = q < Nq && (!CAUSAL || kj <= q + off);
+                            const bool vis = q < Nq && (!kRight || kj <= q + offr) && (!kLeft || kj >= q + offl);
                             if (!vis) sv = -INFINITY;
                         }
                         const float pe = exp2_hw(fmaf(sv, p.scale_log2, -l2[e]));
@@ -288,7 +297,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
 // 3. dQ.  BQ = 128 queries per workgroup (4 waves x 32), BC = 64 keys per
 // step; K and V tiles double-buffered in LDS exactly as in the forward pass.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     constexpr int BQ = 128, BC = 64;
     constexpr int NKK = D / 16;
@@ -302,6 +311,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hg = lane >> 5;
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+    constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
+    const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
+    const int offl = off - (MASK == kMaskWindow ? p.wl : 0);
     const int n_qt = (Nq + BQ - 1) / BQ;
     // query tiles of this workgroup: n-1-j (heavy causal tiles first), then
     // with pairing its mirror j
@@ -326,9 +338,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     const int q0 = qt * BQ;
     const int qw = q0 + wave * 32;
     const int qi = qw + l32;
-    const int kend = CAUSAL ? min(Nk, q0 + BQ + off) : Nk;
+    // key tiles [t_first, ntiles) of this query tile, as in the forward pass
+    const int kend = kRight ? min(Nk, q0 + BQ + offr) : Nk;
     const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
-    const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
+    const int t_first = kLeft ? max(0, q0 + offl) / BC : 0;
+    const int kend_w = kRight ? min(Nk, qw + 32 + offr) : Nk;
+    const int kbeg_w = kLeft ? qw + offl : 0;
 
     // this lane's query: Q and dO as B operands, its LSE2 and D
     bf16x8 qreg[NKK], doreg[NKK];
@@ -353,11 +368,11 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dqacc[db] = zero16();
 
-    if (ntiles > 0) load_tile(0, 0);
+    if (ntiles > t_first) load_tile(t_first * BC, 0);
     // vmcnt(0): Q, dO, LSE2, D registers and the first tiles; then the same
     // mark_loaded as in the dK/dV kernel
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (ntiles > 0) tile_barrier();
+    if (ntiles > t_first) tile_barrier();
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         mark_loaded(qreg[kk]);
@@ -366,14 +381,15 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     mark_loaded(l2);
     mark_loaded(dd);
 
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = t_first; t < ntiles; ++t) {
         const int k0 = t * BC;
-        const char* kbuf = smem + (t & 1) * BUF_BYTES;
+        const int buf = (t - t_first) & 1;
+        const char* kbuf = smem + buf * BUF_BYTES;
         const char* vbuf = kbuf + T_BYTES;
         const bool has_next = t + 1 < ntiles;
-        if (has_next) load_tile(k0 + BC, (t + 1) & 1);
+        if (has_next) load_tile(k0 + BC, (t + 1 - t_first) & 1);
 
-        if (k0 < kend_w) {
+        if (k0 < kend_w && (!kLeft || k0 + BC > kbeg_w)) {
             // ---- S^T = K Q^T, dP^T = V dO^T (lane = query, items = keys) ----
             f32x16 s[NKB], dp[NKB];
 #pragma unroll
@@ -389,7 +405,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
                     dp[kb] = mfma_bf16(tile_read_row<D>(vbuf, kb * 32, kk, lane), doreg[kk], dp[kb]);
                 }
             // ---- dS^T = P * (dP - D), P = 2^(S*scale*log2e - LSE2) ----
-            const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw + off);
+            const bool need_mask = (k0 + BC > Nk) || (kRight && k0 + BC - 1 > qw + offr) ||
+                                   (kLeft && k0 < qw + 31 + offl);
             u32x4 dsw[NKC];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -399,7 +416,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
                     float sv = s[kb][i];
                     if (need_mask) {
                         const int key = k0 + kb * 32 + (i >> 2) * 8 + 4 * hg + (i & 3);
-                        const bool vis = key < Nk && (!CAUSAL || key <= qi + off);
+                        const bool vis = key < Nk && (!kRight || key <= qi + offr) && (!kLeft || key >= qi + offl);
                         if (!vis) sv = -INFINITY;
                     }
                     const float pe = exp2_hw(fmaf(sv, p.scale_log2, -l2));
@@ -439,7 +456,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 template <int D>
-static hipError_t launch_bwd_d(bool causal, const BwdParams& p, hipStream_t s) {
+static const void* bwd_kernel(bool dkdv, int mask) {
+    if (mask == kMaskCausal) return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskCausal> : (const void*)bwd_dq_kernel<D, kMaskCausal>;
+    if (mask == kMaskWindow) return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskWindow> : (const void*)bwd_dq_kernel<D, kMaskWindow>;
+    return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskNone> : (const void*)bwd_dq_kernel<D, kMaskNone>;
+}
+
+template <int D>
+static hipError_t launch_bwd_d(int mask, const BwdParams& p, hipStream_t s) {
     const long rows = (long)p.BH * p.Nq;
     if (rows > 0) {
         constexpr int RPB = 256 / (D / 8);
@@ -458,13 +482,13 @@ static hipError_t launch_bwd_d(bool causal, const BwdParams& p, hipStream_t s) {
     void* args[] = {&pp};
     const long grid_kv = (long)p.BH * p.kv_slots;
     if (grid_kv > 0) {   // with Nq == 0 the walk is empty and dK = dV = 0 are written
-        const void* fn = causal ? (const void*)bwd_dkdv_kernel<D, true> : (const void*)bwd_dkdv_kernel<D, false>;
+        const void* fn = bwd_kernel<D>(true, mask);
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
     const long grid_q = (long)p.BH * p.q_slots;
     if (grid_q > 0) {   // with Nk == 0 every row is empty and dQ = 0 is written
-        const void* fn = causal ? (const void*)bwd_dq_kernel<D, true> : (const void*)bwd_dq_kernel<D, false>;
+        const void* fn = bwd_kernel<D>(false, mask);
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_q), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
@@ -478,8 +502,8 @@ bool bwd_pair_tiles(bool causal, long bh, int n_tiles) {
     return causal && n_tiles >= 2 && n_tiles <= 64 && bh * n_tiles >= 4 * 512;
 }
 
-hipError_t launch_bwd(int d, bool causal, BwdParams p, hipStream_t stream) {
-    return d == 64 ? launch_bwd_d<64>(causal, p, stream) : launch_bwd_d<128>(causal, p, stream);
+hipError_t launch_bwd(int d, int mask, BwdParams p, hipStream_t stream) {
+    return d == 64 ? launch_bwd_d<64>(mask, p, stream) : launch_bwd_d<128>(mask, p, stream);
 }
 
 }  // namespace fa

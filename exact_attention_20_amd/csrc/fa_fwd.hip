@@ -63,7 +63,10 @@ constexpr float kRescaleSlack = 8.0f;
 template <int D>
 constexpr int fwd_waves_per_simd() { return D == 64 ? 4 : 2; }
 
-template <int D, bool CAUSAL, bool SPLIT>
+// MASK: kMaskNone, kMaskCausal (key j visible to query i iff j <= i + off,
+// off = Nk - Nq) or kMaskWindow (iff i + off - wl <= j <= i + off + wr, the
+// reaches p.wl, p.wr; an unbounded side holds kWindowUnbounded).
+template <int D, int MASK, bool SPLIT>
 __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(FwdParams p) {
     constexpr int BR = 128, BC = 64;
     constexpr int NKK = D / 16;        // k-steps over d for S^T
@@ -94,6 +97,10 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     }
     const int n_items = (!SPLIT && p.paired && slot != nqt - 1 - slot) ? 2 : 1;
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+    // right bound: key <= query + offr; left bound (windows): key >= query + offl
+    constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
+    const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
+    const int offl = off - (MASK == kMaskWindow ? p.wl : 0);
     const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
     const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
     const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
@@ -129,9 +136,11 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // Key tiles a query tile needs: causal stops after the last key its last
     // query can see; tiles beyond are skipped entirely.
     auto tiles_of = [&](int qt_) {
-        const int kend_ = CAUSAL ? min(Nk, qt_ * BR + BR + off) : Nk;
+        const int kend_ = kRight ? min(Nk, qt_ * BR + BR + offr) : Nk;
         return kend_ > 0 ? (kend_ + BC - 1) / BC : 0;
     };
+    // first key tile a query tile needs (a window's left bound skips the rest)
+    auto first_tile_of = [&](int qt_) { return kLeft ? max(0, qt_ * BR + offl) / BC : 0; };
 
     int b0 = 0;               // LDS buffer of the current item's first key tile
     bool prefetched = false;  // its Q and first key tile were issued by the previous item
@@ -141,13 +150,14 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     const int qw = q0 + wave * 32;     // this wave's first query
     const int qi = qw + l32;           // this lane's query
     // key tiles [t_lo, t_hi) of this item (a run of them in split-KV mode)
-    const int t_lo = SPLIT ? split * p.tiles_per_split : 0;
+    const int t_lo = SPLIT ? split * p.tiles_per_split : first_tile_of(qt);
     const int t_hi = SPLIT ? min(tiles_of(qt), t_lo + p.tiles_per_split) : tiles_of(qt);
     const int ntiles = t_hi > t_lo ? t_hi - t_lo : 0;
     // last key + 1 this wave sees; a wave whose rows all lie past Nq skips the math
-    const int kend_w = qw >= Nq ? 0 : CAUSAL ? min(Nk, qw + 32 + off) : Nk;
+    const int kend_w = qw >= Nq ? 0 : kRight ? min(Nk, qw + 32 + offr) : Nk;
+    const int kbeg_w = kLeft ? qw + offl : 0;   // first key the wave's first row sees
     const bool more = it + 1 < n_items;
-    const int next_ntiles = more ? tiles_of(slot) : 0;
+    const int next_ntiles = more ? tiles_of(slot) - first_tile_of(slot) : 0;
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -179,9 +189,9 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         // the other buffer takes the next key tile, or the next item's first
         const bool has_next = t + 1 < t_hi || next_ntiles > 0;
         if (t + 1 < t_hi) load_tile(k0 + BC, buf ^ 1);
-        else if (has_next) load_tile(0, buf ^ 1);
+        else if (has_next) load_tile(first_tile_of(slot) * BC, buf ^ 1);
 
-        if (k0 < kend_w) {
+        if (k0 < kend_w && (!kLeft || k0 + BC > kbeg_w)) {
             // ---- S^T = K Q^T (fp32 accumulators) ----
             f32x16 s[NKB];
 #pragma unroll
@@ -207,18 +217,23 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             // ---- mask: only tiles that straddle the diagonal or the tail ----
-            const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw + off);
+            const bool need_mask = (k0 + BC > Nk) || (kRight && k0 + BC - 1 > qw + offr) ||
+                                   (kLeft && k0 < qw + 31 + offl);
             if (need_mask) {
                 // item i of block kb is key k0 + kb*32 + (i/4)*8 + 4*hg + i%4: it is
                 // visible iff its offset within the tile, past 4*hg, is <= lim
-                // (key < Nk and, causal, key <= qi + off): one compare per item
+                // (key < Nk and key <= qi + offr): one compare per item, and for
+                // a window also >= lo (key >= qi + offl)
                 int lim = Nk - 1 - k0 - 4 * hg;
-                if (CAUSAL) lim = min(lim, qi + off - k0 - 4 * hg);
+                if (kRight) lim = min(lim, qi + offr - k0 - 4 * hg);
+                const int lo = kLeft ? qi + offl - k0 - 4 * hg : 0;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) s[kb][i] = -INFINITY;
+                    for (int i = 0; i < 16; ++i) {
+                        const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
+                        if (o > lim || (kLeft && o < lo)) s[kb][i] = -INFINITY;
+                    }
             }
             // ---- online softmax update (base-2, scale folded) ----
             // m_run is the scaling base.  It moves (and O, l are rescaled by
@@ -447,7 +462,7 @@ __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdParams p) {
 // fp32 inputs and output: true fp32 products on the 32x32x2 fp32 MFMA.
 // BR = BC = 64 (2 waves x 32 rows); single-buffered LDS.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdParams p) {
     constexpr int BR = 64, BC = D == 128 ? 32 : 64;   // LDS: K (padded) + V within 64 KiB
     constexpr int NKB = BC / 32, NDB = D / 32;
@@ -467,9 +482,14 @@ __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdParams p) {
     const float* Kh = (const float*)p.k + (size_t)bh * Nk * D;
     const float* Vh = (const float*)p.v + (size_t)bh * Nk * D;
 
-    const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
+    constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
+    const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
+    const int offl = off - (MASK == kMaskWindow ? p.wl : 0);
+    const int kend = kRight ? min(Nk, q0 + BR + offr) : Nk;
     const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
-    const int kend_w = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
+    const int t_first = kLeft ? max(0, q0 + offl) / BC : 0;
+    const int kend_w = kRight ? min(Nk, qw + 32 + offr) : Nk;
+    const int kbeg_w = kLeft ? qw + offl : 0;
 
     float qreg[D / 2];
 #pragma unroll
@@ -480,7 +500,7 @@ __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdParams p) {
     for (int db = 0; db < NDB; ++db) oacc[db] = zero16();
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = t_first; t < ntiles; ++t) {
         const int k0 = t * BC;
         __syncthreads();
         for (int c = tid; c < BC * D / 4; c += 128) {
@@ -498,7 +518,7 @@ __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdParams p) {
             *(f32x4*)(vs + r * D + cc * 4) = vv;
         }
         __syncthreads();
-        if (k0 >= kend_w) continue;
+        if (k0 >= kend_w || (kLeft && k0 + BC <= kbeg_w)) continue;
 
         f32x16 s[NKB];
 #pragma unroll
@@ -509,14 +529,15 @@ __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdParams p) {
             for (int kb = 0; kb < NKB; ++kb)
                 s[kb] = mfma_f32(ks[(kb * 32 + l32) * KS + 2 * kk + hg], qreg[kk], s[kb]);
 
-        const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw + off);
+        const bool need_mask = (k0 + BC > Nk) || (kRight && k0 + BC - 1 > qw + offr) ||
+                               (kLeft && k0 < qw + 31 + offl);
         if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = k0 + kb * 32 + (i >> 2) * 8 + 4 * hg + (i & 3);
-                    const bool vis = key < Nk && (!CAUSAL || key <= qi + off);
+                    const bool vis = key < Nk && (!kRight || key <= qi + offr) && (!kLeft || key >= qi + offl);
                     if (!vis) s[kb][i] = -INFINITY;
                 }
         }
@@ -596,31 +617,32 @@ static hipError_t launch(KernelT kernel, int grid, int block, const FwdParams& p
     return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(block), args, 0, s);
 }
 
-hipError_t launch_fwd(int dtype, int d, bool causal, int BH, FwdParams p, hipStream_t stream) {
+template <int MASK>
+static hipError_t launch_fwd_mask(int dtype, int d, const FwdParams& p, hipStream_t stream) {
     const int grid = p.total_wg;
-    (void)BH;
-    if (grid == 0) return hipSuccess;
-    if (dtype == 1) {
-        if (d == 64) return causal ? launch(fwd_bf16_kernel<64, true, false>, grid, 256, p, stream)
-                                   : launch(fwd_bf16_kernel<64, false, false>, grid, 256, p, stream);
-        return causal ? launch(fwd_bf16_kernel<128, true, false>, grid, 256, p, stream)
-                      : launch(fwd_bf16_kernel<128, false, false>, grid, 256, p, stream);
-    }
-    if (d == 64) return causal ? launch(fwd_f32_kernel<64, true>, grid, 128, p, stream)
-                               : launch(fwd_f32_kernel<64, false>, grid, 128, p, stream);
-    return causal ? launch(fwd_f32_kernel<128, true>, grid, 128, p, stream)
-                  : launch(fwd_f32_kernel<128, false>, grid, 128, p, stream);
+    if (dtype == 1)
+        return d == 64 ? launch(fwd_bf16_kernel<64, MASK, false>, grid, 256, p, stream)
+                       : launch(fwd_bf16_kernel<128, MASK, false>, grid, 256, p, stream);
+    return d == 64 ? launch(fwd_f32_kernel<64, MASK>, grid, 128, p, stream)
+                   : launch(fwd_f32_kernel<128, MASK>, grid, 128, p, stream);
+}
+
+hipError_t launch_fwd(int dtype, int d, int mask, FwdParams p, hipStream_t stream) {
+    if (p.total_wg == 0) return hipSuccess;
+    if (mask == kMaskCausal) return launch_fwd_mask<kMaskCausal>(dtype, d, p, stream);
+    if (mask == kMaskWindow) return launch_fwd_mask<kMaskWindow>(dtype, d, p, stream);
+    return launch_fwd_mask<kMaskNone>(dtype, d, p, stream);
 }
 
 hipError_t launch_fwd_split(int d, bool causal, FwdParams p, hipStream_t stream) {
     if (p.total_wg == 0) return hipSuccess;
     hipError_t e;
     if (d == 64)
-        e = causal ? launch(fwd_bf16_kernel<64, true, true>, p.total_wg, 256, p, stream)
-                   : launch(fwd_bf16_kernel<64, false, true>, p.total_wg, 256, p, stream);
+        e = causal ? launch(fwd_bf16_kernel<64, kMaskCausal, true>, p.total_wg, 256, p, stream)
+                   : launch(fwd_bf16_kernel<64, kMaskNone, true>, p.total_wg, 256, p, stream);
     else
-        e = causal ? launch(fwd_bf16_kernel<128, true, true>, p.total_wg, 256, p, stream)
-                   : launch(fwd_bf16_kernel<128, false, true>, p.total_wg, 256, p, stream);
+        e = causal ? launch(fwd_bf16_kernel<128, kMaskCausal, true>, p.total_wg, 256, p, stream)
+                   : launch(fwd_bf16_kernel<128, kMaskNone, true>, p.total_wg, 256, p, stream);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((long)p.BH * p.Nq);
     return d == 64 ? launch(fwd_combine_kernel<64>, grid, 256, p, stream)

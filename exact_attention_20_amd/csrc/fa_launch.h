@@ -7,6 +7,17 @@
 
 namespace fa {
 
+// Masks of the forward and backward kernels.
+//   kMaskNone:   every key is visible;
+//   kMaskCausal: key j is visible to query i iff j <= i + (Nk - Nq);
+//   kMaskWindow: iff i + off - wl <= j <= i + off + wr, off = Nk - Nq, with
+//                the reaches wl, wr >= 0 in the params; a side without a
+//                bound holds kWindowUnbounded (large enough that every
+//                sequence fits inside it, small enough that no offset sum
+//                overflows: |off| <= FA_MAX_SEQ = 2^23).
+enum { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
+constexpr int kWindowUnbounded = 1 << 28;
+
 struct FwdParams {
     const void* q;
     const void* k;
@@ -20,6 +31,7 @@ struct FwdParams {
     int paired;        // bf16 kernel: a workgroup runs query tiles n-1-j and j of one head
     int total_wg;      // B * H * n_slots (split-KV: B * H * n_qtiles * n_splits)
     float scale_log2;  // scale * log2(e)
+    int wl, wr;        // window reaches (kMaskWindow only)
     // split-KV mode only
     int BH;
     int n_splits;         // runs of key tiles per query tile
@@ -49,6 +61,7 @@ struct BwdParams {
     int q_paired;
     float scale;
     float scale_log2;
+    int wl, wr;        // window reaches (kMaskWindow only)
 };
 
 // Query rows per forward workgroup for a dtype (used to size the grid).
@@ -61,9 +74,9 @@ bool fwd_pair_tiles(int dtype, int d, bool causal, long bh, int n_qtiles);
 // The same decision for the backward kernels' key and query tiles.
 bool bwd_pair_tiles(bool causal, long bh, int n_tiles);
 
-hipError_t launch_fwd(int dtype, int d, bool causal, int BH, FwdParams p, hipStream_t stream);
+hipError_t launch_fwd(int dtype, int d, int mask, FwdParams p, hipStream_t stream);
 // bf16 split-KV forward: partial kernel, then the combine kernel.
 hipError_t launch_fwd_split(int d, bool causal, FwdParams p, hipStream_t stream);
-hipError_t launch_bwd(int d, bool causal, BwdParams p, hipStream_t stream);
+hipError_t launch_bwd(int d, int mask, BwdParams p, hipStream_t stream);
 
 }  // namespace fa

@@ -69,7 +69,8 @@ typedef enum {
     FA_ERR_ALIGN = -5,      /* a tensor pointer is not 16-byte aligned       */
     FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required       */
     FA_ERR_LAUNCH = -7,     /* the HIP runtime refused a kernel launch       */
-    FA_ERR_SCALE = -8       /* scale is not finite or not > 0                */
+    FA_ERR_SCALE = -8,      /* scale is not finite or not > 0                */
+    FA_ERR_WINDOW = -9      /* a window reach below -1                       */
 } fa_status_t;
 
 /* Largest Nq or Nk accepted (keeps every in-head byte offset within 32 bits). */
@@ -150,6 +151,37 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dO, void* dq, void* dk, void* dv,
            int B, int H, int Nq, int Nk, int d, float scale, int causal,
            int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Local (sliding-window) attention.  The tiled forward of "01 · IO-awareness、
+ * online softmax 与 tiling" §3 applies a mask to each score block before the
+ * online update and names sliding windows among its masks; the pages fix no
+ * formula for one.  The reading taken here extends the causal rule above:
+ * with off = Nk - Nq, key j is visible to query i iff
+ *
+ *     i + off - window_left  <=  j  <=  i + off + window_right,
+ *
+ * each reach >= 0, or -1 for a side with no bound (FA_ERR_WINDOW below -1).
+ * (-1, 0) is exactly the causal mask and (-1, -1) no mask: those calls run
+ * the causal / unmasked kernels and give bitwise the results of fa_fwd /
+ * fa_bwd with causal = 1 / 0.  A sliding window of W keys ending at the
+ * diagonal is (W - 1, 0).  Key tiles wholly outside a query tile's window
+ * are skipped, so the work scales with the visible pairs.  A row with no
+ * visible key gets O = 0 and LSE = -inf, as under the causal mask.
+ *
+ * Arguments, layouts, ownership, dtypes, determinism and errors are those
+ * of fa_fwd and fa_bwd, with (window_left, window_right) in place of causal.
+ * fa_bwd_window must be given the window its forward pass used.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int d, float scale,
+                  int window_left, int window_right, int dtype, void* stream);
+
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                  int B, int H, int Nq, int Nk, int d, float scale,
+                  int window_left, int window_right, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* A static, human-readable description of a status code. */
 const char* fa_strerror(int status);

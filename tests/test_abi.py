@@ -36,13 +36,14 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
     assert set(syms) == {"fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
-                         "fa_bwd_workspace_bytes", "fa_strerror"}
+                         "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_bwd_window",
+                         "fa_strerror"}
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_strerror_covers_codes():
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         msg = fa.fa_strerror(code)
         assert msg and msg != "unknown status", code
     assert fa.fa_strerror(-99) == "unknown status"
@@ -161,3 +162,37 @@ def test_splitkv_validation_codes():
     assert split(workspace=FAKE_MIS) == -5
     assert split(B=0) == 0
     assert split(Nq=0) == 0
+
+
+def fwdw(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=16, Nk=16, d=64,
+             scale=0.125, window_left=8, window_right=0, dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_window(**a)
+
+
+def bwdw(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dO=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             B=1, H=2, Nq=32, Nk=32, d=64, scale=0.125, window_left=8, window_right=4,
+             dtype=fa.FA_BF16, workspace=FAKE, workspace_bytes=1 << 20, stream=0)
+    a.update(kw)
+    return fa.fa_bwd_window(**a)
+
+
+def test_window_validation_codes():
+    # a reach below -1 is rejected before anything else is looked at
+    assert fwdw(window_left=-2) == -9
+    assert fwdw(window_right=-5, q=0) == -9
+    assert bwdw(window_left=-2) == -9
+    assert bwdw(window_right=-2, dtype=fa.FA_F32) == -9
+    # the shared checks still apply to every window, bounded or not
+    for wl, wr in ((8, 0), (-1, 0), (-1, -1), (0, 0), (3, -1), (1 << 30, 1 << 30)):
+        assert fwdw(window_left=wl, window_right=wr, d=96) == -3
+        assert fwdw(window_left=wl, window_right=wr, q=0) == -1
+        assert fwdw(window_left=wl, window_right=wr, k=FAKE_MIS) == -5
+        assert fwdw(window_left=wl, window_right=wr, scale=0.0) == -8
+        assert fwdw(window_left=wl, window_right=wr, B=0, q=0, k=0, v=0, o=0, lse=0) == 0
+        assert bwdw(window_left=wl, window_right=wr, dtype=fa.FA_F32) == -4
+        assert bwdw(window_left=wl, window_right=wr, workspace=0) == -6
+        assert bwdw(window_left=wl, window_right=wr, dk=0) == -1
+        assert bwdw(window_left=wl, window_right=wr, B=0) == 0

@@ -30,6 +30,7 @@ class Workload:
     causal: bool
     backward: bool = False
     seed: int = 0
+    window: tuple | None = None   # local window (wl, wr), None sides unbounded; replaces causal
 
     @property
     def scale(self) -> float:
@@ -37,6 +38,8 @@ class Workload:
 
     def describe(self) -> str:
         mode = "causal" if self.causal else "non-causal"
+        if self.window is not None:
+            mode = f"window {self.window}"
         bwd = ", fwd+bwd" if self.backward else ""
         return (f"B={self.B} H={self.H} Nq={self.Nq} Nk={self.Nk} d={self.d} "
                 f"{self.dtype} {mode}{bwd}")
@@ -55,7 +58,13 @@ TRAIN_STEP = Workload("train_step_bf16", 4, 16, 4096, 4096, 64, "bf16", True, ba
 # Nq = 1 with bottom-right causal alignment sees every key.
 DECODE = Workload("decode_bf16", 1, 32, 1, 32768, 128, "bf16", True, seed=1006)
 
-ALL = [SINGLE_HEAD, GPT2_SMALL, LLAMA_CAUSAL, LONG_CONTEXT, TRAIN_STEP, DECODE]
+# Local attention over the long-context shape: every query sees itself and
+# the 4095 keys before it (a sliding window of 4096 keys ending at the
+# diagonal), so the work is 1/8 of the causal case's.
+SLIDING_WINDOW = Workload("sliding_window_bf16", 1, 32, 32768, 32768, 128, "bf16", False,
+                          seed=1007, window=(4095, 0))
+
+ALL = [SINGLE_HEAD, GPT2_SMALL, LLAMA_CAUSAL, LONG_CONTEXT, TRAIN_STEP, DECODE, SLIDING_WINDOW]
 
 
 def torch_dtype(name: str) -> torch.dtype:
