@@ -25,6 +25,8 @@ from .attention import (  # noqa: F401
     attention_forward,
     attention_forward_rows,
     attention_backward,
+    varlen_forward,
+    varlen_backward,
     online_rescale,
     tiled_forward,
     tiled_forward_renormalised,

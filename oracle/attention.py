@@ -28,7 +28,13 @@ Readings taken where the pages are silent or disagree:
     extension of the causal rule (causal is (None, 0), a sliding window of W
     keys is (W - 1, 0));
   * a query row with no visible key has O = 0 and LSE = -inf, and contributes
-    nothing to the gradients.
+    nothing to the gradients;
+  * a variable-length batch packs each head's sequences along the token axis,
+    [H, T, d] with sequence b at rows cu[b] .. cu[b+1]-1; every sequence
+    attends within itself under the causal or window rule taken over its own
+    lengths: the pages name variable-length masks but fix no layout, and
+    head-major packing keeps each head's rows contiguous as the fixed-length
+    [B, H, N, d] layout does.
 """
 
 from __future__ import annotations
@@ -183,6 +189,57 @@ def attention_backward(q, k, v, do, scale: float, causal: bool, window=None):
         dk[ix] = scale * (dS.T @ q[ix])
         O[ix], L[ix], D[ix] = Oh, Lh, Dh
     return dq, dk, dvv, O, L, D
+
+
+# ----------------------------------------------------------------------------
+# variable-length batches (packed sequences)
+# ----------------------------------------------------------------------------
+def _sequence_bounds(cu, total: int, name: str) -> np.ndarray:
+    """Validated offsets: cu[0] = 0, non-decreasing, cu[-1] <= total."""
+    cu = np.asarray(cu, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] > total:
+        raise ValueError(f"{name} must start at 0, never decrease and end at most at {total}")
+    return cu
+
+
+def varlen_forward(q, k, v, cu_q, cu_k, scale: float, causal: bool, window=None):
+    """A batch of B sequences of different lengths, packed along the token
+    axis ([P2] §3 lists variable-length batches among the masks of its tiled
+    forward; the pages fix no layout).  q [H, Tq, d] holds sequence b's query
+    rows at cu_q[b] .. cu_q[b+1]-1, k and v [H, Tk, d] its keys at
+    cu_k[b] .. cu_k[b+1]-1.  Each sequence attends only within itself, with
+    the causal or window rule of ``visible_mask`` taken over its own lengths
+    (offset Lk_b - Lq_b).  Rows outside every sequence have no defined value
+    and are returned as NaN.  Returns (O [H, Tq, dv], LSE [H, Tq])."""
+    q, k, v = _as_f64(q, k, v)
+    H, Tq = q.shape[0], q.shape[1]
+    cu_q = _sequence_bounds(cu_q, Tq, "cu_q")
+    cu_k = _sequence_bounds(cu_k, k.shape[1], "cu_k")
+    if cu_q.size != cu_k.size:
+        raise ValueError("cu_q and cu_k must describe the same number of sequences")
+    O = np.full((H, Tq, v.shape[-1]), np.nan)
+    L = np.full((H, Tq), np.nan)
+    for b in range(cu_q.size - 1):
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        O[:, qs], L[:, qs] = attention_forward(q[:, qs], k[:, ks], v[:, ks], scale, causal, window)
+    return O, L
+
+
+def varlen_backward(q, k, v, do, cu_q, cu_k, scale: float, causal: bool, window=None):
+    """Gradients of sum(dO * O) for ``varlen_forward``: each sequence's
+    gradients are those of ``attention_backward`` on its own rows; rows
+    outside every sequence are NaN.  Returns (dq, dk, dv)."""
+    q, k, v, do = _as_f64(q, k, v, do)
+    cu_q = _sequence_bounds(cu_q, q.shape[1], "cu_q")
+    cu_k = _sequence_bounds(cu_k, k.shape[1], "cu_k")
+    if cu_q.size != cu_k.size:
+        raise ValueError("cu_q and cu_k must describe the same number of sequences")
+    dq, dk, dvv = np.full_like(q, np.nan), np.full_like(k, np.nan), np.full_like(v, np.nan)
+    for b in range(cu_q.size - 1):
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        dq[:, qs], dk[:, ks], dvv[:, ks], *_ = attention_backward(
+            q[:, qs], k[:, ks], v[:, ks], do[:, qs], scale, causal, window)
+    return dq, dk, dvv
 
 
 # ----------------------------------------------------------------------------

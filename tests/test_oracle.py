@@ -516,3 +516,111 @@ def test_window_flop_count_matches_mask():
     for (Nq, Nk, window) in [(64, 64, (15, 0)), (30, 70, (3, 5)), (70, 30, (None, 2)), (33, 33, (4, None))]:
         pairs = int(visible_mask(Nq, Nk, False, window=window).sum())
         assert oracle.attention_flops(2, 3, Nq, Nk, 16, False, window=window) == 4 * 16 * pairs * 6
+
+
+# ------------------------------------------------------- variable-length batches
+def _packed(r, lens_q, lens_k, H=2, d=6, pad_q=0, pad_k=0):
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int64)
+    Tq, Tk = int(cu_q[-1]) + pad_q, int(cu_k[-1]) + pad_k
+    q = r.standard_normal((H, Tq, d))
+    k = r.standard_normal((H, Tk, d))
+    v = r.standard_normal((H, Tk, d))
+    do = r.standard_normal((H, Tq, d))
+    return q, k, v, do, cu_q, cu_k
+
+
+def _block_mask(cu_q, cu_k, causal, window):
+    """True = visible, built key by key over the whole packed batch: the key
+    must belong to the query's own sequence, and inside it pass the causal or
+    window bound measured from that sequence's bottom-right diagonal."""
+    Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+    wl, wr = (None, 0) if causal else (window if window is not None else (None, None))
+    vis = torch.zeros(Tq, Tk, dtype=torch.bool)
+    for b in range(len(cu_q) - 1):
+        lq, lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for i in range(lq):
+            for j in range(lk):
+                diag = i + lk - lq
+                if (wr is None or j <= diag + wr) and (wl is None or j >= diag - wl):
+                    vis[cu_q[b] + i, cu_k[b] + j] = True
+    return vis
+
+
+VARLEN = [
+    # query lengths, key lengths, causal, window
+    ([5, 1, 9], [5, 1, 9], True, None),
+    ([4, 7, 3], [6, 2, 8], False, None),
+    ([3, 8, 6], [9, 5, 6], True, None),          # Nq != Nk both ways: empty rows
+    ([6, 6, 10], [6, 9, 4], False, (2, 1)),
+    ([0, 5, 4], [3, 0, 4], False, (None, 0)),    # empty sequences on either side
+]
+
+
+@pytest.mark.parametrize("lens_q,lens_k,causal,window", VARLEN)
+def test_varlen_forward_matches_block_masked_torch(lens_q, lens_k, causal, window):
+    # one attention over the whole packed batch with a block-diagonal mask,
+    # through torch's fp64 softmax and logsumexp (a library routine)
+    r = rng(40 + sum(lens_q))
+    q, k, v, _, cu_q, cu_k = _packed(r, lens_q, lens_k)
+    O, L = oracle.varlen_forward(q, k, v, cu_q, cu_k, 0.45, causal, window)
+    vis = _block_mask(cu_q, cu_k, causal, window)
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    s = ((tq @ tk.transpose(-1, -2)) * 0.45).masked_fill(~vis, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    p = torch.nan_to_num(torch.softmax(s, dim=-1), nan=0.0)   # rows with no key: P = 0
+    ref = p @ tv
+    assert np.max(np.abs(O - ref.numpy())) <= 1e-12
+    fin = np.isfinite(lse.numpy())
+    assert np.array_equal(np.isfinite(L), fin)
+    assert np.max(np.abs(L[fin] - lse.numpy()[fin]), initial=0.0) <= 1e-12
+    assert np.all(O[~np.broadcast_to(fin[..., None], O.shape)] == 0.0)
+
+
+@pytest.mark.parametrize("lens_q,lens_k,causal,window", VARLEN[:4])
+def test_varlen_backward_matches_block_masked_autograd(lens_q, lens_k, causal, window):
+    r = rng(60 + sum(lens_k))
+    q, k, v, do, cu_q, cu_k = _packed(r, lens_q, lens_k)
+    dq, dk, dvv = oracle.varlen_backward(q, k, v, do, cu_q, cu_k, 0.3, causal, window)
+    vis = _block_mask(cu_q, cu_k, causal, window)
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    s = ((tq @ tk.transpose(-1, -2)) * 0.3).masked_fill(~vis, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    p = torch.where(vis.any(dim=-1, keepdim=True), p, torch.zeros_like(p))
+    (p @ tv).backward(torch.from_numpy(do))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dvv, tv.grad)):
+        assert np.max(np.abs(mine - ref.numpy())) <= 1e-12
+
+
+def test_varlen_equal_lengths_is_the_fixed_length_batch():
+    r = rng(70)
+    B, H, N, d = 3, 2, 11, 5
+    q, k, v = (r.standard_normal((B, H, N, d)) for _ in range(3))
+    O, L = attention_forward(q, k, v, 0.5, True)
+    pack = lambda x: x.transpose(1, 0, 2, 3).reshape(H, B * N, d)   # [B,H,N,d] -> [H, B*N, d]
+    cu = np.arange(B + 1) * N
+    Ov, Lv = oracle.varlen_forward(pack(q), pack(k), pack(v), cu, cu, 0.5, True)
+    assert np.array_equal(Ov, pack(O))
+    assert np.array_equal(Lv, L.transpose(1, 0, 2).reshape(H, B * N))
+
+
+def test_varlen_sequence_order_and_padding():
+    r = rng(71)
+    lens = [4, 9, 2]
+    q, k, v, _, cu, _ = _packed(r, lens, lens, pad_q=3, pad_k=2)
+    O, L = oracle.varlen_forward(q, k, v, cu, cu, 0.6, True)
+    # trailing rows outside every sequence have no value
+    assert np.all(np.isnan(O[:, cu[-1]:])) and np.all(np.isnan(L[:, cu[-1]:]))
+    # reversing the order of the sequences reverses the order of their outputs
+    order = [2, 1, 0]
+    seg = lambda x, b: x[:, cu[b]:cu[b + 1]]
+    q2, k2, v2 = (np.concatenate([seg(x, b) for b in order], axis=1) for x in (q, k, v))
+    cu2 = np.concatenate([[0], np.cumsum([lens[b] for b in order])])
+    O2, L2 = oracle.varlen_forward(q2, k2, v2, cu2, cu2, 0.6, True)
+    for pos, b in enumerate(order):
+        assert np.array_equal(O2[:, cu2[pos]:cu2[pos + 1]], seg(O, b))
+        assert np.array_equal(L2[:, cu2[pos]:cu2[pos + 1]], seg(L, b))
+    with pytest.raises(ValueError):
+        oracle.varlen_forward(q, k, v, [0, 5, 3], [0, 5, 3], 0.6, True)
+    with pytest.raises(ValueError):
+        oracle.varlen_forward(q, k, v, [1, 5], [1, 5], 0.6, True)
