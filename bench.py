@@ -90,17 +90,22 @@ def traffic_for(workload_name: str):
     return entry.get("hbm_bytes_per_launch")
 
 
+def blas_threads() -> int:
+    """Threads of the BLAS the oracle's NumPy products run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(blas) if blas else 1
+    except Exception:
+        return 1
+
+
 def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     """Time the fp64 oracle (as it stands) on whole heads of the workload until
     about ``target_s`` seconds of CPU work; report its causal-adjusted rate."""
     import numpy as np
     from oracle import attention_forward
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-        threads = max(blas) if blas else 1
-    except Exception:
-        threads = 1
+    threads = blas_threads()
     per_head_flops = fwd_flops(w) / (w.B * w.H)
     done, t_total = 0, 0.0
     heads = w.B * w.H
@@ -185,6 +190,91 @@ def train_step_timing(fa, wl, steps: int, warmup: int, window=None):
             "bwd_flops": 10 * w.d * pairs,
             "note": "bwd = prep (D, LSE*log2e) + dK/dV kernel + dQ kernel; 10*d FLOPs per "
                     "visible pair"}
+
+
+def bench_varlen(fa, wl, w, args) -> dict:
+    """One fa_fwd_varlen launch over the packed variable-length workload per
+    step, timed like the fixed-length line; FLOPs are 4*d per visible pair
+    summed over the sequences."""
+    import torch
+    dev = torch.device("cuda:0")
+    L = w.lengths()
+    q, k, v, cu_q, cu_k = wl.varlen_workload_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    cq, ck = cu_q.to(dev), cu_k.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.H, qd.shape[1]), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    T = qd.shape[1]
+    mask = (-1, 0) if w.causal else (-1, -1)
+    argv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            cq.data_ptr(), ck.data_ptr(), len(L), w.H, T, T, max(L), max(L), w.d, w.scale,
+            mask[0], mask[1], fa.FA_BF16, stream.cuda_stream)
+
+    def step():
+        st = fa.fa_fwd_varlen(*argv)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd_varlen")
+
+    ms = time_launches(step, stream, args.steps, args.warmup)
+    pairs = sum(visible_pairs(n, n, w.causal) for n in L)
+    flops = 4 * w.d * pairs * w.H
+    tflops = flops / (ms * 1e-3) / 1e12
+    nbytes = w.H * (4 * T * w.d * 2 + 4 * T)
+    result = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded iid N(0,1) inputs; seeded log-uniform sequence lengths)",
+        "config": {"workload": w.name, "sequences": len(L), "min_len": min(L), "max_len": max(L),
+                   "total_tokens": T, "H": w.H, "d": w.d, "causal": w.causal, "lse_saved": True,
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK[w.dtype],
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK[w.dtype], 4),
+                     "traffic": traffic_for(w.name)},
+        "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "peak_GBps": 8000.0, "note": "algorithmic bytes / launch time, warm caches"},
+    }
+    if not args.no_train_step:
+        # fa_bwd_varlen on the same packed batch (dO drawn after the inputs)
+        g = torch.Generator(device="cpu").manual_seed(w.seed + 1)
+        do = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        need = fa.fa_bwd_varlen_workspace_bytes(w.H, T, w.d, fa.FA_BF16)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        step()
+        bargv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()) + argv[5:17] + \
+                (fa.FA_BF16, ws.data_ptr(), need, stream.cuda_stream)
+
+        def bwd():
+            st = fa.fa_bwd_varlen(*bargv)
+            if st != 0:
+                raise fa.FAError(st, "fa_bwd_varlen")
+
+        ms_b = time_launches(bwd, stream, 20, 5)
+        result["backward"] = {"bwd_ms": round(ms_b, 5),
+                              "bwd_tflops": round(10 * w.d * pairs * w.H / ms_b / 1e9, 3),
+                              "note": "fa_bwd_varlen: prep + dK/dV + dQ; 10*d FLOPs per visible pair"}
+    if not args.no_cpu_baseline:
+        from oracle import attention_forward
+        # whole (head, sequence) pairs, head by head, until ~15 s of CPU work
+        done, t_total, done_pairs = 0, 0.0, 0
+        while done < w.H * len(L) and t_total < 15.0:
+            h, b = divmod(done, len(L))
+            s, e = int(cu_q[b]), int(cu_q[b + 1])
+            t0 = time.perf_counter()
+            attention_forward(q[h, s:e].double().numpy(), k[h, s:e].double().numpy(),
+                              v[h, s:e].double().numpy(), w.scale, w.causal)
+            t_total += time.perf_counter() - t0
+            done_pairs += visible_pairs(L[b], L[b], w.causal)
+            done += 1
+        result["cpu_baseline"] = {
+            "value": round(4 * w.d * done_pairs / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {w.H * len(L)} (head, sequence) pairs, fp64 NumPy, "
+                      f"{t_total:.1f} s; numpy exp single-threaded"}
+    return result
 
 
 def _counter_means(csv_dir: str, counter: str):
@@ -281,10 +371,13 @@ def main():
     import exact_attention_20_amd as fa
     import workloads as wl
 
-    w = {x.name: x for x in wl.ALL}[args.workload]
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload == wl.VARLEN_CAUSAL.name:
+        print(json.dumps(bench_varlen(fa, wl, wl.VARLEN_CAUSAL, args)), flush=True)
+        return
+    w = {x.name: x for x in wl.ALL}[args.workload]
     dev = torch.device("cuda:0")
     q, k, v = wl.workload_inputs(w)[:3]
     qd, kd, vd = (t.to(dev) for t in (q, k, v))

@@ -17,6 +17,13 @@ Raw entry points, same names and argument order as ``include/fa.h``:
                   dtype, stream) -> int
     fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, window_left,
                   window_right, dtype, workspace, workspace_bytes, stream) -> int
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, d, scale, window_left, window_right, dtype,
+                  stream) -> int
+    fa_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, H,
+                  total_q, total_k, max_seqlen_q, max_seqlen_k, d, scale, window_left,
+                  window_right, dtype, workspace, workspace_bytes, stream) -> int
+    fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype) -> int
     fa_strerror(status) -> str
 (pointer arguments are integers: device addresses, 0 for NULL)
 
@@ -26,9 +33,16 @@ non-zero status:
     attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0) -> (o, lse)
     attention_backward(q, k, v, o, lse, do, scale=None, causal=False, window=None)
         -> (dq, dk, dv)
+    attention_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                             max_seqlen_k, scale=None, causal=False, window=None) -> (o, lse)
+    attention_backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                              max_seqlen_k, scale=None, causal=False, window=None)
+        -> (dq, dk, dv)
 ``window`` is a local window (wl, wr): key j is visible to query i iff
 i + (Nk - Nq) - wl <= j <= i + (Nk - Nq) + wr, a side None for no bound; it
-replaces ``causal`` (giving both raises ValueError).
+replaces ``causal`` (giving both raises ValueError).  The varlen helpers take
+head-major packed tensors q, o [H, total_q, d], k, v [H, total_k, d] and int32
+device offsets cu_seqlens [B+1]; every sequence attends within itself.
 """
 
 from __future__ import annotations
@@ -40,7 +54,9 @@ import os
 __all__ = [
     "FA_F32", "FA_BF16", "FAError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_bwd_window", "fa_strerror",
+    "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_bwd_window", "fa_fwd_varlen",
+    "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_strerror",
+    "attention_forward_varlen", "attention_backward_varlen",
     "attention_forward", "attention_forward_splitkv", "attention_backward",
 ]
 
@@ -88,6 +104,13 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i,
                                   vp, sz, vp]
     lib.fa_bwd_window.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_fwd_varlen.restype = i
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                  f, i, i, i, vp, sz, vp]
+    lib.fa_bwd_varlen.restype = i
+    lib.fa_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_varlen_workspace_bytes.restype = sz
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -138,6 +161,30 @@ def fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, windo
                                         _p(dk), _p(dv), B, H, Nq, Nk, d, float(scale),
                                         int(window_left), int(window_right), int(dtype),
                                         _p(workspace), int(workspace_bytes), _p(stream))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, d, scale, window_left, window_right, dtype,
+                  stream) -> int:
+    return load_library().fa_fwd_varlen(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(cu_seqlens_q),
+                                        _p(cu_seqlens_k), B, H, total_q, total_k, max_seqlen_q,
+                                        max_seqlen_k, d, float(scale), int(window_left),
+                                        int(window_right), int(dtype), _p(stream))
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, H, total_q,
+                  total_k, max_seqlen_q, max_seqlen_k, d, scale, window_left, window_right,
+                  dtype, workspace, workspace_bytes, stream) -> int:
+    return load_library().fa_bwd_varlen(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
+                                        _p(dk), _p(dv), _p(cu_seqlens_q), _p(cu_seqlens_k), B, H,
+                                        total_q, total_k, max_seqlen_q, max_seqlen_k, d,
+                                        float(scale), int(window_left), int(window_right),
+                                        int(dtype), _p(workspace), int(workspace_bytes),
+                                        _p(stream))
+
+
+def fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype) -> int:
+    return int(load_library().fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype))
 
 
 def fa_strerror(status: int) -> str:
@@ -276,4 +323,90 @@ def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=
         st = fa_bwd_window(*ptrs, B, H, Nq, Nk, d, scale, w[0], w[1], code, *ws, _stream())
     if st != 0:
         raise FAError(st, "fa_bwd" if w is None else "fa_bwd_window")
+    return dq, dk, dv
+
+
+def _mask_args(causal, window):
+    """(window_left, window_right) of the C ABI for a causal flag or a window."""
+    w = _window_args(causal, window)
+    if w is not None:
+        return w
+    return (-1, 0) if causal else (-1, -1)
+
+
+def _check_cu(cu, name, B, dev):
+    import torch
+    if not cu.is_cuda or cu.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() != B + 1 or not cu.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor of B + 1 = {B + 1} offsets")
+
+
+def attention_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                             scale=None, causal=False, window=None, out=None, lse=None):
+    """Attention over a packed variable-length batch via fa_fwd_varlen (bf16).
+
+    q [H, total_q, d], k and v [H, total_k, d] (head-major packing); sequence b
+    owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and the matching
+    key rows; every length must be at most max_seqlen_q / max_seqlen_k.
+    Returns (o [H, total_q, d], lse [H, total_q]); rows outside every
+    sequence are left as they were in ``out`` / ``lse`` (uninitialised when
+    those are not given).
+    """
+    import torch
+    H, Tq, d = q.shape
+    Tk = k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    _check(q, "q", (H, Tq, d), q.dtype)
+    _check(k, "k", (H, Tk, d), q.dtype)
+    _check(v, "v", (H, Tk, d), q.dtype)
+    _check_cu(cu_seqlens_q, "cu_seqlens_q", B, q.device)
+    _check_cu(cu_seqlens_k, "cu_seqlens_k", B, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", (H, Tq, d), q.dtype)
+    if lse is None:
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    _check(lse, "lse", (H, Tq), torch.float32)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    wl, wr = _mask_args(causal, window)
+    st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Tq, Tk,
+                       int(max_seqlen_q), int(max_seqlen_k), d, scale, wl, wr, _dtype_code(q),
+                       _stream())
+    if st != 0:
+        raise FAError(st, "fa_fwd_varlen")
+    return out, lse
+
+
+def attention_backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                              max_seqlen_k, scale=None, causal=False, window=None,
+                              workspace=None):
+    """dq, dk, dv of sum(do * o) for ``attention_forward_varlen`` via
+    fa_bwd_varlen (bf16); the same packing, offsets and mask as the forward."""
+    import torch
+    H, Tq, d = q.shape
+    Tk = k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    for t, n, s in ((q, "q", (H, Tq, d)), (k, "k", (H, Tk, d)), (v, "v", (H, Tk, d)),
+                    (o, "o", (H, Tq, d)), (do, "do", (H, Tq, d))):
+        _check(t, n, s, q.dtype)
+    _check(lse, "lse", (H, Tq), torch.float32)
+    _check_cu(cu_seqlens_q, "cu_seqlens_q", B, q.device)
+    _check_cu(cu_seqlens_k, "cu_seqlens_k", B, q.device)
+    code = _dtype_code(q)
+    need = fa_bwd_varlen_workspace_bytes(H, Tq, d, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    wl, wr = _mask_args(causal, window)
+    st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Tq, Tk,
+                       int(max_seqlen_q), int(max_seqlen_k), d, scale, wl, wr, code,
+                       workspace.data_ptr() if workspace is not None else 0,
+                       workspace.numel() if workspace is not None else 0, _stream())
+    if st != 0:
+        raise FAError(st, "fa_bwd_varlen")
     return dq, dk, dv

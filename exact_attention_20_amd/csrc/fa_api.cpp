@@ -202,7 +202,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o,
 
     const size_t rows = (size_t)BH * Nq;
     const size_t vec_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
-    fa::BwdParams p;
+    fa::BwdParams p = {};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -227,7 +227,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o,
     p.scale_log2 = scale * 1.44269504088896340736f;
     p.wl = mask.wl;
     p.wr = mask.wr;
-    return hip_status(fa::launch_bwd(d, mask.mode, p, (hipStream_t)stream));
+    return hip_status(fa::launch_bwd(d, mask.mode, false, p, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -265,6 +265,139 @@ extern "C" int fa_bwd_window(const void* q, const void* k, const void* v, const 
     if (st != FA_OK) return st;
     return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, m, dtype, workspace,
                     workspace_bytes, stream);
+}
+
+namespace {
+
+// Checks of a variable-length call's sizes, head dim, dtype (bf16 only),
+// scale and offset pointers.  Leaves *work = false when there is nothing
+// to compute.
+int check_varlen(const int* cu_q, const int* cu_k, int B, int H, int total_q, int total_k,
+                 int max_q, int max_k, int d, float scale, int dtype, bool* work) {
+    if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0) return FA_ERR_SHAPE;
+    if (max_q > FA_MAX_SEQ || max_k > FA_MAX_SEQ) return FA_ERR_SHAPE;
+    const long double elems = (long double)H * (total_q > total_k ? total_q : total_k) * 128.0L;
+    if (elems > 4.0e18L) return FA_ERR_SHAPE;
+    // grids: B*H workgroups per 64 rows of the longest sequence, and the
+    // backward pre-pass over H*total_q rows
+    if ((long double)B * H * ((max_q > max_k ? max_q : max_k) / 64 + 2) > 2.0e9L) return FA_ERR_SHAPE;
+    if ((long double)H * total_q > 2.0e11L) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    *work = B > 0 && H > 0;
+    if (*work && (!cu_q || !cu_k)) return FA_ERR_NULL;
+    if (*work && (!aligned4(cu_q) || !aligned4(cu_k))) return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+fa::VarlenParams varlen_params(const int* cu_q, const int* cu_k, int B, int H, int total_q,
+                               int total_k, int max_q, int max_k) {
+    fa::VarlenParams v;
+    v.cu_q = cu_q;
+    v.cu_k = cu_k;
+    v.B = B;
+    v.H = H;
+    v.total_q = total_q;
+    v.total_k = total_k;
+    v.max_q = max_q;
+    v.max_k = max_k;
+    return v;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                             int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                             float scale, int window_left, int window_right, int dtype, void* stream) {
+    Mask m;
+    int st = window_mask(window_left, window_right, &m);
+    if (st != FA_OK) return st;
+    bool work = false;
+    st = check_varlen(cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                      d, scale, dtype, &work);
+    if (st != FA_OK) return st;
+    if (!work || total_q == 0 || max_seqlen_q == 0) return FA_OK;
+    if (!q || !o || (total_k > 0 && (!k || !v))) return FA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(o) || (total_k > 0 && (!aligned16(k) || !aligned16(v)))) return FA_ERR_ALIGN;
+    if (lse && !aligned4(lse)) return FA_ERR_ALIGN;
+
+    fa::FwdParams p = {};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.n_slots = (max_seqlen_q + 127) / 128;   // query tiles of the longest sequence
+    p.n_qtiles = p.n_slots;
+    p.paired = 0;
+    p.total_wg = (int)((long)B * H * p.n_slots);
+    p.scale_log2 = scale * 1.44269504088896340736f;
+    p.wl = m.wl;
+    p.wr = m.wr;
+    p.vl = varlen_params(cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k);
+    return hip_status(fa::launch_fwd_varlen(d, m.mode, p, (hipStream_t)stream));
+}
+
+extern "C" size_t fa_bwd_varlen_workspace_bytes(int H, int total_q, int d, int dtype) {
+    // the same two row vectors as fa_bwd's, over the H * total_q packed rows
+    if (H < 0 || total_q < 0 || (d != 64 && d != 128) || dtype != FA_BF16) return 0;
+    if ((long double)H * total_q > 2.0e11L) return 0;
+    const size_t rows = (size_t)H * total_q;
+    const size_t vec = (rows * sizeof(float) + 255) & ~(size_t)255;
+    return 2 * vec;
+}
+
+extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                             const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                             int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                             float scale, int window_left, int window_right, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    Mask m;
+    int st = window_mask(window_left, window_right, &m);
+    if (st != FA_OK) return st;
+    bool work = false;
+    st = check_varlen(cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                      d, scale, dtype, &work);
+    if (st != FA_OK) return st;
+    if (!work || (total_q == 0 && total_k == 0)) return FA_OK;
+    const bool has_q = total_q > 0, has_k = total_k > 0;
+    if ((has_q && (!q || !o || !lse || !dO || !dq)) || (has_k && (!k || !v || !dk || !dv))) return FA_ERR_NULL;
+    if (has_q && (!aligned16(q) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) || !aligned4(lse)))
+        return FA_ERR_ALIGN;
+    if (has_k && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))) return FA_ERR_ALIGN;
+    const size_t need = fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
+
+    const size_t rows = (size_t)H * total_q;
+    const size_t vec_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
+    fa::BwdParams p = {};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.dO = dO;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.lse2 = (float*)workspace;
+    p.dvec = (float*)((char*)workspace + vec_bytes);
+    p.BH = (int)((long)B * H);
+    // workgroups per (batch, head): tiles of the longest sequence, unpaired
+    p.kv_slots = (max_seqlen_k + 127) / 128;
+    p.q_slots = (max_seqlen_q + 127) / 128;
+    p.kv_paired = 0;
+    p.q_paired = 0;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.44269504088896340736f;
+    p.wl = m.wl;
+    p.wr = m.wr;
+    p.vl = varlen_params(cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k);
+    return hip_status(fa::launch_bwd(d, m.mode, true, p, (hipStream_t)stream));
 }
 
 extern "C" const char* fa_strerror(int status) {

@@ -77,7 +77,7 @@ __device__ __forceinline__ void pack_pairs(const float (&x)[16], u32x4& lo, u32x
 // values of LSE*log2e and D; two stages, the next one filled while the
 // current one is used.
 // ---------------------------------------------------------------------------
-template <int D, int MASK>
+template <int D, int MASK, bool VARLEN = false>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParams p) {
     constexpr int BKV = 128, BQ = 64;
     constexpr int NQB = BQ / 32;              // 32-query blocks per step
@@ -91,24 +91,31 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hg = lane >> 5;
-    const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+    // key tiles of this workgroup: j (ascending j = heavy causal tiles
+    // first), then with pairing its mirror n-1-j (equal causal work per
+    // workgroup)
+    int bh, slot;
+    if (VARLEN) varlen_slot(p.vl, p.kv_slots, blockIdx.x, bh, slot);
+    else map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, slot);
+    // the (batch, head) pair's lengths and first rows (variable-length
+    // batches: its own sequence's; a workgroup past its key tiles exits)
+    SeqGeometry sg;
+    if constexpr (VARLEN) sg = seq_geometry(p.vl, bh);
+    else sg = SeqGeometry{p.Nq, p.Nk, (size_t)bh * p.Nq, (size_t)bh * p.Nk};
+    const int Nq = sg.Nq, Nk = sg.Nk, off = Nk - Nq;
     // query q sees key j iff j <= q + offr (causal, windows) and, for a
     // window, j >= q + offl (the mask family of the forward kernels)
     constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
     const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
     const int offl = off - (MASK == kMaskWindow ? p.wl : 0);
     const int n_kt = (Nk + BKV - 1) / BKV;
-    // key tiles of this workgroup: j (ascending j = heavy causal tiles
-    // first), then with pairing its mirror n-1-j (equal causal work per
-    // workgroup)
-    int bh, slot;
-    map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, slot);
+    if (VARLEN && slot >= n_kt) return;
     const int n_items = (p.kv_paired && slot != n_kt - 1 - slot) ? 2 : 1;
 
-    const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
-    const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
-    const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
-    const bf16* dOh = (const bf16*)p.dO + (size_t)bh * Nq * D;
+    const bf16* Qh = (const bf16*)p.q + sg.q_row0 * D;
+    const bf16* Kh = (const bf16*)p.k + sg.k_row0 * D;
+    const bf16* Vh = (const bf16*)p.v + sg.k_row0 * D;
+    const bf16* dOh = (const bf16*)p.dO + sg.q_row0 * D;
 
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (uint32_t)Nk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, (uint32_t)Nk * D * 2);
@@ -152,8 +159,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
     // one step ahead into registers and written to the stage's LDS slot just
     // before the end-of-step barrier.  Rows past Nq get LSE2 = +inf (P = 0).
     static_assert(BQ == 64, "one query per lane of wave 0");
-    const float* L2h = p.lse2 + (size_t)bh * Nq;
-    const float* Dh = p.dvec + (size_t)bh * Nq;
+    const float* L2h = p.lse2 + sg.q_row0;
+    const float* Dh = p.dvec + sg.q_row0;
     float nl2 = INFINITY, ndd = 0.f;
     auto fetch_vec = [&](int qt) {
         const int q = qt * BQ + lane;
@@ -274,8 +281,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
 
     // ---- dK = scale * dK^T, dV = dV^T (lane = key, items = d) ----
     if (kj < Nk) {
-        bf16* dKr = (bf16*)p.dk + (size_t)bh * Nk * D + (size_t)kj * D;
-        bf16* dVr = (bf16*)p.dv + (size_t)bh * Nk * D + (size_t)kj * D;
+        bf16* dKr = (bf16*)p.dk + sg.k_row0 * D + (size_t)kj * D;
+        bf16* dVr = (bf16*)p.dv + sg.k_row0 * D + (size_t)kj * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -297,7 +304,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
 // 3. dQ.  BQ = 128 queries per workgroup (4 waves x 32), BC = 64 keys per
 // step; K and V tiles double-buffered in LDS exactly as in the forward pass.
 // ---------------------------------------------------------------------------
-template <int D, int MASK>
+template <int D, int MASK, bool VARLEN = false>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     constexpr int BQ = 128, BC = 64;
     constexpr int NKK = D / 16;
@@ -310,21 +317,26 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hg = lane >> 5;
-    const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+    // query tiles of this workgroup: n-1-j (heavy causal tiles first), then
+    // with pairing its mirror j
+    int bh, slot;
+    if (VARLEN) varlen_slot(p.vl, p.q_slots, blockIdx.x, bh, slot);
+    else map_head_tile(blockIdx.x, p.BH * p.q_slots, p.q_slots, bh, slot);
+    SeqGeometry sg;
+    if constexpr (VARLEN) sg = seq_geometry(p.vl, bh);
+    else sg = SeqGeometry{p.Nq, p.Nk, (size_t)bh * p.Nq, (size_t)bh * p.Nk};
+    const int Nq = sg.Nq, Nk = sg.Nk, off = Nk - Nq;
     constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
     const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
     const int offl = off - (MASK == kMaskWindow ? p.wl : 0);
     const int n_qt = (Nq + BQ - 1) / BQ;
-    // query tiles of this workgroup: n-1-j (heavy causal tiles first), then
-    // with pairing its mirror j
-    int bh, slot;
-    map_head_tile(blockIdx.x, p.BH * p.q_slots, p.q_slots, bh, slot);
+    if (VARLEN && slot >= n_qt) return;
     const int n_items = (p.q_paired && slot != n_qt - 1 - slot) ? 2 : 1;
 
-    const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
-    const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
-    const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
-    const bf16* dOh = (const bf16*)p.dO + (size_t)bh * Nq * D;
+    const bf16* Qh = (const bf16*)p.q + sg.q_row0 * D;
+    const bf16* Kh = (const bf16*)p.k + sg.k_row0 * D;
+    const bf16* Vh = (const bf16*)p.v + sg.k_row0 * D;
+    const bf16* dOh = (const bf16*)p.dO + sg.q_row0 * D;
 
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, (uint32_t)Nq * D * 2);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dOh, (uint32_t)Nq * D * 2);
@@ -355,8 +367,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     }
     float l2 = INFINITY, dd = 0.f;             // rows past Nq: P = 0
     if (qi < Nq) {
-        l2 = p.lse2[(size_t)bh * Nq + qi];
-        dd = p.dvec[(size_t)bh * Nq + qi];
+        l2 = p.lse2[sg.q_row0 + qi];
+        dd = p.dvec[sg.q_row0 + qi];
     }
 
     auto load_tile = [&](int k0, int buf) {
@@ -440,7 +452,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 
     // ---- dQ = scale * dQ^T (lane = query, items = d) ----
     if (qi < Nq) {
-        bf16* dQr = (bf16*)p.dq + (size_t)bh * Nq * D + (size_t)qi * D;
+        bf16* dQr = (bf16*)p.dq + sg.q_row0 * D + (size_t)qi * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -455,16 +467,24 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool VARLEN>
 static const void* bwd_kernel(bool dkdv, int mask) {
-    if (mask == kMaskCausal) return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskCausal> : (const void*)bwd_dq_kernel<D, kMaskCausal>;
-    if (mask == kMaskWindow) return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskWindow> : (const void*)bwd_dq_kernel<D, kMaskWindow>;
-    return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskNone> : (const void*)bwd_dq_kernel<D, kMaskNone>;
+    if (mask == kMaskCausal)
+        return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskCausal, VARLEN> : (const void*)bwd_dq_kernel<D, kMaskCausal, VARLEN>;
+    if (mask == kMaskWindow)
+        return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskWindow, VARLEN> : (const void*)bwd_dq_kernel<D, kMaskWindow, VARLEN>;
+    return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskNone, VARLEN> : (const void*)bwd_dq_kernel<D, kMaskNone, VARLEN>;
 }
 
 template <int D>
-static hipError_t launch_bwd_d(int mask, const BwdParams& p, hipStream_t s) {
-    const long rows = (long)p.BH * p.Nq;
+static const void* bwd_kernel(bool dkdv, int mask, bool varlen) {
+    return varlen ? bwd_kernel<D, true>(dkdv, mask) : bwd_kernel<D, false>(dkdv, mask);
+}
+
+template <int D>
+static hipError_t launch_bwd_d(int mask, bool varlen, const BwdParams& p, hipStream_t s) {
+    // the pre-pass runs over every query row: B*H*Nq, or H*total_q packed
+    const long rows = varlen ? (long)p.vl.H * p.vl.total_q : (long)p.BH * p.Nq;
     if (rows > 0) {
         constexpr int RPB = 256 / (D / 8);
         const long grid = (rows + RPB - 1) / RPB;
@@ -482,13 +502,13 @@ static hipError_t launch_bwd_d(int mask, const BwdParams& p, hipStream_t s) {
     void* args[] = {&pp};
     const long grid_kv = (long)p.BH * p.kv_slots;
     if (grid_kv > 0) {   // with Nq == 0 the walk is empty and dK = dV = 0 are written
-        const void* fn = bwd_kernel<D>(true, mask);
+        const void* fn = bwd_kernel<D>(true, mask, varlen);
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
     const long grid_q = (long)p.BH * p.q_slots;
     if (grid_q > 0) {   // with Nk == 0 every row is empty and dQ = 0 is written
-        const void* fn = bwd_kernel<D>(false, mask);
+        const void* fn = bwd_kernel<D>(false, mask, varlen);
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_q), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
@@ -502,8 +522,8 @@ bool bwd_pair_tiles(bool causal, long bh, int n_tiles) {
     return causal && n_tiles >= 2 && n_tiles <= 64 && bh * n_tiles >= 4 * 512;
 }
 
-hipError_t launch_bwd(int d, int mask, BwdParams p, hipStream_t stream) {
-    return d == 64 ? launch_bwd_d<64>(mask, p, stream) : launch_bwd_d<128>(mask, p, stream);
+hipError_t launch_bwd(int d, int mask, bool varlen, BwdParams p, hipStream_t stream) {
+    return d == 64 ? launch_bwd_d<64>(mask, varlen, p, stream) : launch_bwd_d<128>(mask, varlen, p, stream);
 }
 
 }  // namespace fa

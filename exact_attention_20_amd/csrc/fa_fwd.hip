@@ -66,7 +66,10 @@ constexpr int fwd_waves_per_simd() { return D == 64 ? 4 : 2; }
 // MASK: kMaskNone, kMaskCausal (key j visible to query i iff j <= i + off,
 // off = Nk - Nq) or kMaskWindow (iff i + off - wl <= j <= i + off + wr, the
 // reaches p.wl, p.wr; an unbounded side holds kWindowUnbounded).
-template <int D, int MASK, bool SPLIT>
+// VARLEN: the (batch, head) pair's lengths and rows come from the packed
+// variable-length batch in p.vl; n_slots then counts the query tiles of the
+// longest sequence, and a workgroup past its own sequence's tiles exits.
+template <int D, int MASK, bool SPLIT, bool VARLEN = false>
 __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(FwdParams p) {
     constexpr int BR = 128, BC = 64;
     constexpr int NKK = D / 16;        // k-steps over d for S^T
@@ -86,24 +89,31 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // j of the same head (causal: the two tiles together see n+1 rows of key
     // tiles whatever j is, so every workgroup gets the same work).
     int bh, slot, split = 0;
-    const int nqt = p.n_qtiles;
     if (SPLIT) {
         int r;
-        map_head_tile(blockIdx.x, p.total_wg, nqt * p.n_splits, bh, r);
-        slot = nqt - 1 - r / p.n_splits;   // so that tile n-1-slot is tile r / n_splits
+        map_head_tile(blockIdx.x, p.total_wg, p.n_qtiles * p.n_splits, bh, r);
+        slot = p.n_qtiles - 1 - r / p.n_splits;   // so that tile n-1-slot is tile r / n_splits
         split = r % p.n_splits;
+    } else if (VARLEN) {
+        varlen_slot(p.vl, p.n_slots, blockIdx.x, bh, slot);
     } else {
         map_head_tile(blockIdx.x, p.total_wg, p.n_slots, bh, slot);
     }
+    // the (batch, head) pair's lengths and first rows in the [rows, D] views
+    SeqGeometry sg;
+    if constexpr (VARLEN) sg = seq_geometry(p.vl, bh);
+    else sg = SeqGeometry{p.Nq, p.Nk, (size_t)bh * p.Nq, (size_t)bh * p.Nk};
+    const int Nq = sg.Nq, Nk = sg.Nk, off = Nk - Nq;
+    const int nqt = VARLEN ? (Nq + BR - 1) / BR : p.n_qtiles;
+    if (VARLEN && slot >= nqt) return;   // past the sequence's last query tile
     const int n_items = (!SPLIT && p.paired && slot != nqt - 1 - slot) ? 2 : 1;
-    const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
     // right bound: key <= query + offr; left bound (windows): key >= query + offl
     constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
     const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
     const int offl = off - (MASK == kMaskWindow ? p.wl : 0);
-    const bf16* Qh = (const bf16*)p.q + (size_t)bh * Nq * D;
-    const bf16* Kh = (const bf16*)p.k + (size_t)bh * Nk * D;
-    const bf16* Vh = (const bf16*)p.v + (size_t)bh * Nk * D;
+    const bf16* Qh = (const bf16*)p.q + sg.q_row0 * D;
+    const bf16* Kh = (const bf16*)p.k + sg.k_row0 * D;
+    const bf16* Vh = (const bf16*)p.v + sg.k_row0 * D;
 
     // Buffer resources over this head's Q, K and V: rows past Nq / Nk read as
     // zero, so ragged tails need no branches.
@@ -365,7 +375,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
             }
         constexpr int CPR = D / 8;          // 16-byte chunks per row
         constexpr int RPI = 64 / CPR;       // rows per 64-lane pass
-        bf16* Ow = (bf16*)p.o + (size_t)bh * Nq * D + (size_t)qw * D;
+        bf16* Ow = (bf16*)p.o + sg.q_row0 * D + (size_t)qw * D;
 #pragma unroll
         for (int r0 = 0; r0 < 32; r0 += RPI) {
             const int r = r0 + lane / CPR, c = lane % CPR;
@@ -373,7 +383,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
             if (qw + r < Nq) *(u32x4*)(Ow + (size_t)r * D + c * 8) = x;
         }
     } else if (qi < Nq) {
-        bf16* Oh = (bf16*)p.o + (size_t)bh * Nq * D + (size_t)qi * D;
+        bf16* Oh = (bf16*)p.o + sg.q_row0 * D + (size_t)qi * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -385,7 +395,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
             }
     }
     if (qi < Nq && hg == 0 && p.lse)
-        p.lse[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        p.lse[sg.q_row0 + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     if (kStageO && more) {
         // every wave has read its staged rows before the buffer takes the
         // next item's Q tile (or, unprefetched, that item's own copies)
@@ -632,6 +642,19 @@ hipError_t launch_fwd(int dtype, int d, int mask, FwdParams p, hipStream_t strea
     if (mask == kMaskCausal) return launch_fwd_mask<kMaskCausal>(dtype, d, p, stream);
     if (mask == kMaskWindow) return launch_fwd_mask<kMaskWindow>(dtype, d, p, stream);
     return launch_fwd_mask<kMaskNone>(dtype, d, p, stream);
+}
+
+hipError_t launch_fwd_varlen(int d, int mask, FwdParams p, hipStream_t stream) {
+    if (p.total_wg == 0) return hipSuccess;
+    const int g = p.total_wg;
+    if (d == 64) {
+        if (mask == kMaskCausal) return launch(fwd_bf16_kernel<64, kMaskCausal, false, true>, g, 256, p, stream);
+        if (mask == kMaskWindow) return launch(fwd_bf16_kernel<64, kMaskWindow, false, true>, g, 256, p, stream);
+        return launch(fwd_bf16_kernel<64, kMaskNone, false, true>, g, 256, p, stream);
+    }
+    if (mask == kMaskCausal) return launch(fwd_bf16_kernel<128, kMaskCausal, false, true>, g, 256, p, stream);
+    if (mask == kMaskWindow) return launch(fwd_bf16_kernel<128, kMaskWindow, false, true>, g, 256, p, stream);
+    return launch(fwd_bf16_kernel<128, kMaskNone, false, true>, g, 256, p, stream);
 }
 
 hipError_t launch_fwd_split(int d, bool causal, FwdParams p, hipStream_t stream) {

@@ -18,6 +18,24 @@ namespace fa {
 enum { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
 constexpr int kWindowUnbounded = 1 << 28;
 
+// A variable-length batch: B sequences packed along the token axis of
+// head-major tensors (q, o, dO, dq: [H, total_q, d]; k, v, dk, dv:
+// [H, total_k, d]; lse and the backward row vectors: [H, total_q]).
+// Sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 and key rows
+// cu_k[b] .. cu_k[b+1]-1 of every head.  A workgroup finds its (batch,
+// head) pair and tile with varlen_slot() and its sequence's lengths and
+// first rows with seq_geometry() (fa_device.h).
+struct VarlenParams {
+    const int* cu_q;   // [B+1] device offsets of the query rows
+    const int* cu_k;   // [B+1] device offsets of the key rows
+    int B;             // sequences
+    int H;             // heads
+    int total_q;       // packed query rows per head
+    int total_k;       // packed key rows per head
+    int max_q;         // bound on every sequence's query count (sizes the grid)
+    int max_k;         // bound on every sequence's key count
+};
+
 struct FwdParams {
     const void* q;
     const void* k;
@@ -38,6 +56,7 @@ struct FwdParams {
     int tiles_per_split;  // 64-key tiles per run
     float* o_part;        // [n_splits, B*H, Nq, d] fp32 partial outputs
     float* lse_part;      // [n_splits, B*H, Nq] fp32 partial LSE, log2 units
+    VarlenParams vl;      // variable-length mode only
 };
 
 struct BwdParams {
@@ -62,6 +81,7 @@ struct BwdParams {
     float scale;
     float scale_log2;
     int wl, wr;        // window reaches (kMaskWindow only)
+    VarlenParams vl;   // variable-length mode only
 };
 
 // Query rows per forward workgroup for a dtype (used to size the grid).
@@ -75,8 +95,12 @@ bool fwd_pair_tiles(int dtype, int d, bool causal, long bh, int n_qtiles);
 bool bwd_pair_tiles(bool causal, long bh, int n_tiles);
 
 hipError_t launch_fwd(int dtype, int d, int mask, FwdParams p, hipStream_t stream);
+// bf16 forward over a variable-length batch (p.vl); grid B*H*n_slots.
+hipError_t launch_fwd_varlen(int d, int mask, FwdParams p, hipStream_t stream);
 // bf16 split-KV forward: partial kernel, then the combine kernel.
 hipError_t launch_fwd_split(int d, bool causal, FwdParams p, hipStream_t stream);
-hipError_t launch_bwd(int d, int mask, BwdParams p, hipStream_t stream);
+// varlen: the kernels take each (batch, head)'s geometry from p.vl; the
+// row-wise pre-pass covers all H * total_q packed rows.
+hipError_t launch_bwd(int d, int mask, bool varlen, BwdParams p, hipStream_t stream);
 
 }  // namespace fa

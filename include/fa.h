@@ -183,6 +183,50 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
                   int window_left, int window_right, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Variable-length (packed) batches.  The tiled forward of "01 · IO-awareness、
+ * online softmax 与 tiling" §3 lists variable-length batches among the masks
+ * it applies to each score block; the pages fix no layout.  Here B sequences
+ * of different lengths are packed along the token axis of head-major tensors:
+ *
+ *   q, o, dO, dq: [H, total_q, d];  k, v, dk, dv: [H, total_k, d];
+ *   lse: [H, total_q] (float32, natural log);
+ *   cu_seqlens_q, cu_seqlens_k: int32 [B+1] device arrays; sequence b owns
+ *   query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows
+ *   cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of every head.
+ *
+ * Every sequence attends only within itself, with the mask taken over its
+ * own lengths (off = Lk_b - Lq_b in the rules above).  The mask is a window
+ * pair as in fa_fwd_window: (-1, -1) none, (-1, 0) causal, else a local
+ * window.  max_seqlen_q and max_seqlen_k (<= FA_MAX_SEQ) must bound every
+ * sequence's lengths; they size the grids.  The offsets must start at 0,
+ * never decrease and end at most at total_q / total_k; the kernels clamp
+ * offsets into [0, total] and lengths to the maxima, so inconsistent offsets
+ * cannot cause an access outside the tensors, but the results of such
+ * sequences are unspecified.  Rows outside every sequence (past
+ * cu_seqlens[B]) are not written.  Since the host never reads the offsets,
+ * they may be produced on the stream just before the call.
+ *
+ * Only FA_BF16 (FA_ERR_DTYPE otherwise).  Deterministic.  B, H or total_q
+ * equal to 0 is a no-op that returns FA_OK.  fa_bwd_varlen's workspace: at
+ * least fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype) bytes (the two
+ * row vectors of fa_bwd over the H * total_q packed rows); the same mask and
+ * offsets as the forward call must be given.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                  int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                  float scale, int window_left, int window_right, int dtype, void* stream);
+
+size_t fa_bwd_varlen_workspace_bytes(int H, int total_q, int d, int dtype);
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                  int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                  float scale, int window_left, int window_right, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* fa_strerror(int status);
 

@@ -37,6 +37,7 @@ def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
     assert set(syms) == {"fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
                          "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_bwd_window",
+                         "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes",
                          "fa_strerror"}
     for s in syms:
         assert hasattr(lib, s), s
@@ -196,3 +197,60 @@ def test_window_validation_codes():
         assert bwdw(window_left=wl, window_right=wr, workspace=0) == -6
         assert bwdw(window_left=wl, window_right=wr, dk=0) == -1
         assert bwdw(window_left=wl, window_right=wr, B=0) == 0
+
+
+def fwdv(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu_seqlens_q=FAKE, cu_seqlens_k=FAKE,
+             B=3, H=2, total_q=100, total_k=120, max_seqlen_q=50, max_seqlen_k=60, d=64,
+             scale=0.125, window_left=-1, window_right=0, dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_varlen(**a)
+
+
+def bwdv(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dO=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, B=3, H=2, total_q=100, total_k=120,
+             max_seqlen_q=50, max_seqlen_k=60, d=128, scale=0.125, window_left=-1,
+             window_right=-1, dtype=fa.FA_BF16, workspace=FAKE, workspace_bytes=1 << 20, stream=0)
+    a.update(kw)
+    return fa.fa_bwd_varlen(**a)
+
+
+def test_varlen_validation_codes():
+    for call in (fwdv, bwdv):
+        assert call(window_left=-2) == -9
+        assert call(B=-1) == -2
+        assert call(total_q=-1) == -2
+        assert call(max_seqlen_k=-1) == -2
+        assert call(max_seqlen_q=(1 << 23) + 1) == -2
+        assert call(d=96) == -3
+        assert call(dtype=fa.FA_F32) == -4
+        assert call(dtype=5) == -4
+        assert call(scale=0.0) == -8
+        assert call(cu_seqlens_q=0) == -1
+        assert call(cu_seqlens_k=0) == -1
+        assert call(cu_seqlens_k=FAKE + 2) == -5
+        assert call(q=0) == -1
+        assert call(v=FAKE_MIS) == -5
+        # nothing to compute: no pointer is looked at
+        assert call(B=0, q=0, k=0, v=0, o=0, lse=0, cu_seqlens_q=0, cu_seqlens_k=0) == 0
+        assert call(H=0, q=0, cu_seqlens_q=0) == 0
+    assert fwdv(total_q=0, q=0, o=0) == 0
+    assert fwdv(lse=FAKE + 2) == -5
+    assert bwdv(lse=0) == -1
+    assert bwdv(dk=FAKE_MIS) == -5
+    assert bwdv(workspace=0) == -6
+    need = fa.fa_bwd_varlen_workspace_bytes(2, 100, 128, fa.FA_BF16)
+    assert need == 2 * 1024                 # 2 heads x 100 rows x 4 B -> 800 -> 1024, twice
+    assert bwdv(workspace_bytes=need - 1) == -6
+    assert bwdv(total_q=0, total_k=0, q=0, k=0) == 0
+
+
+def test_varlen_workspace_bytes():
+    assert fa.fa_bwd_varlen_workspace_bytes(16, 4096 * 4, 64, fa.FA_BF16) == 2 * 16 * 4096 * 4 * 4
+    assert fa.fa_bwd_varlen_workspace_bytes(1, 3, 64, fa.FA_BF16) == 512
+    assert fa.fa_bwd_varlen_workspace_bytes(1, 3, 64, fa.FA_F32) == 0
+    assert fa.fa_bwd_varlen_workspace_bytes(1, 3, 80, fa.FA_BF16) == 0
+    assert fa.fa_bwd_varlen_workspace_bytes(-1, 3, 64, fa.FA_BF16) == 0
+    # more rows per head than FA_MAX_SEQ are fine when packed
+    assert fa.fa_bwd_varlen_workspace_bytes(2, 1 << 24, 64, fa.FA_BF16) == 2 * 2 * (1 << 24) * 4

@@ -67,6 +67,76 @@ SLIDING_WINDOW = Workload("sliding_window_bf16", 1, 32, 32768, 32768, 128, "bf16
 ALL = [SINGLE_HEAD, GPT2_SMALL, LLAMA_CAUSAL, LONG_CONTEXT, TRAIN_STEP, DECODE, SLIDING_WINDOW]
 
 
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed variable-length batch: ``n_seq`` sequences whose lengths are
+    drawn log-uniformly in [lo, hi] (seeded), every head's tokens packed
+    head-major [H, total, d]; queries and keys have the same lengths."""
+    name: str
+    n_seq: int
+    lo: int
+    hi: int
+    H: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def lengths(self):
+        return varlen_lengths(self.n_seq, self.lo, self.hi, self.seed)
+
+    def describe(self) -> str:
+        L = self.lengths()
+        mode = "causal" if self.causal else "non-causal"
+        return (f"{self.n_seq} sequences of {min(L)}..{max(L)} tokens (total {sum(L)}) H={self.H} "
+                f"d={self.d} {self.dtype} {mode}, packed")
+
+
+# A packed batch of 32 sequences of 64..8192 tokens (log-uniform mix, as in
+# a batch of documents of very different lengths), causal, at the
+# Llama-shaped head count and head dimension.
+VARLEN_CAUSAL = VarlenWorkload("varlen_causal_bf16", 32, 64, 8192, 32, 128, "bf16", True, seed=1008)
+
+
+def varlen_lengths(n: int, lo: int, hi: int, seed: int):
+    """``n`` sequence lengths in [lo, hi], log-uniform, from a seeded CPU
+    generator (the same draw on every machine)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    u = torch.rand(n, generator=g, dtype=torch.float64)
+    L = torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))
+    return [int(x) for x in torch.clamp(torch.round(L), lo, hi).tolist()]
+
+
+def make_varlen_inputs(lens_q, lens_k, H: int, d: int, dtype: str, seed: int,
+                       with_do: bool = False, pad_q: int = 0, pad_k: int = 0):
+    """Seeded packed tensors q [H, Tq, d], k, v [H, Tk, d] (and do [H, Tq, d])
+    plus int32 CPU offsets cu_q, cu_k; ``pad_q``/``pad_k`` rows past the last
+    sequence are drawn too.  Same recipe as ``make_inputs``."""
+    cu_q = torch.tensor([0] + list(torch.cumsum(torch.tensor(lens_q, dtype=torch.int64), 0).tolist()),
+                        dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(torch.cumsum(torch.tensor(lens_k, dtype=torch.int64), 0).tolist()),
+                        dtype=torch.int32)
+    Tq, Tk = int(cu_q[-1]) + pad_q, int(cu_k[-1]) + pad_k
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn(H, Tq, d, generator=g, dtype=torch.float32)
+    k = torch.randn(H, Tk, d, generator=g, dtype=torch.float32)
+    v = torch.randn(H, Tk, d, generator=g, dtype=torch.float32)
+    out = [q, k, v]
+    if with_do:
+        out.append(torch.randn(H, Tq, d, generator=g, dtype=torch.float32))
+    td = torch_dtype(dtype)
+    return [t.to(td).contiguous() for t in out] + [cu_q, cu_k]
+
+
+def varlen_workload_inputs(w: VarlenWorkload):
+    L = w.lengths()
+    return make_varlen_inputs(L, L, w.H, w.d, w.dtype, w.seed)
+
+
 def torch_dtype(name: str) -> torch.dtype:
     return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
 
