@@ -17,6 +17,8 @@ write O and LSE) per launch and the rate they are moved at; ``cold`` (with
 --cold, and always for the short-sequence GPT-2-shaped workload) repeats the
 timing one launch at a time after flushing L2 and the Infinity Cache.
 ``train_step`` times fa_fwd and fa_bwd on the training-step workload.
+``mfma_ceiling`` times an 8192^3 bf16 torch.matmul (hipBLASLt) on the same GPU:
+the MFMA rate the vendor library sustains, as context for ``roofline.frac``.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -192,6 +194,24 @@ def train_step_timing(fa, wl, steps: int, warmup: int, window=None):
                     "visible pair"}
 
 
+def gemm_ceiling(n: int = 8192, iters: int = 20) -> dict:
+    """Context for the roofline: the bf16 MFMA rate the vendor library itself
+    sustains on this GPU, one n x n x n torch.matmul (hipBLASLt) timed with HIP
+    events.  The published 2.5 PFLOP/s assumes the 2.4 GHz peak clock, which
+    a chip running MFMAs flat out does not hold."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(0)
+    a = torch.randn(n, n, generator=g).to(torch.bfloat16).to(dev)
+    b = torch.randn(n, n, generator=g).to(torch.bfloat16).to(dev)
+    c = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    ms = time_launches(lambda: torch.matmul(a, b, out=c), stream, iters, 3)
+    del a, b, c
+    return {"op": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt)", "ms": round(ms, 4),
+            "tflops": round(2 * n ** 3 / ms / 1e9, 1)}
+
+
 def bench_varlen(fa, wl, w, args) -> dict:
     """One fa_fwd_varlen launch over the packed variable-length workload per
     step, timed like the fixed-length line; FLOPs are 4*d per visible pair
@@ -235,6 +255,10 @@ def bench_varlen(fa, wl, w, args) -> dict:
         "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "peak_GBps": 8000.0, "note": "algorithmic bytes / launch time, warm caches"},
     }
+    if not args.no_gemm_ceiling:
+        gc = gemm_ceiling()
+        gc["value_over_gemm"] = round(tflops / gc["tflops"], 4)
+        result["mfma_ceiling"] = gc
     if not args.no_train_step:
         # fa_bwd_varlen on the same packed batch (dO drawn after the inputs)
         g = torch.Generator(device="cpu").manual_seed(w.seed + 1)
@@ -334,6 +358,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train-step", action="store_true",
                     help="skip the forward+backward timing on the training-step workload")
+    ap.add_argument("--no-gemm-ceiling", action="store_true",
+                    help="skip the vendor-GEMM reference rate reported beside the roofline")
     ap.add_argument("--cold", action="store_true",
                     help="also time launches one by one after flushing L2 and the Infinity Cache "
                          "(a 512 MiB write before each); on by default for the short-sequence "
@@ -489,6 +515,10 @@ def main():
         result["cold"] = {"ms_median": round(cms, 5), "tflops": round(flops / (cms * 1e-3) / 1e12, 3),
                           "achieved_GBps": round(nbytes / (cms * 1e-3) / 1e9, 1), "launches": len(times),
                           "note": "L2 and Infinity Cache flushed before each launch"}
+    if w.dtype == "bf16" and not args.no_gemm_ceiling:
+        gc = gemm_ceiling()
+        gc["value_over_gemm"] = round(tflops / gc["tflops"], 4) if not decode else None
+        result["mfma_ceiling"] = gc
     if not args.no_train_step:
         result["train_step"] = train_step_timing(fa, wl, steps=20, warmup=5)
         if w.window is not None:
