@@ -52,6 +52,17 @@ __device__ __forceinline__ void map_workgroup(int w, int total, int n_qtiles, in
 // and l are rescaled: P values stay <= 2^8, far inside bf16 and fp32 range.
 constexpr float kRescaleSlack = 8.0f;
 
+// Fast path of the online softmax: once every row of a wave has a scaling
+// base (set by the wave's first key tile with the row maximum), later tiles
+// keep that base and skip the row maximum.  Any base gives the same O / l
+// and m + log l in exact arithmetic; in floating point P, l and O~ keep their
+// relative precision whatever the base, so the only hazard of a base below
+// the true maximum is overflow.  A row whose lane-local running sum ends the
+// query tile outside [0, kFastSumLimit] (overflow, or NaN inputs) marks the
+// wave, and the workgroup then recomputes the query tile with the per-tile
+// maximum and the conditional rescale above.
+constexpr float kFastSumLimit = 0x1p64f;
+
 // SPLIT: split-KV mode.  The key tiles of each query tile are divided into
 // p.n_splits runs of p.tiles_per_split tiles, one workgroup per (batch*head,
 // query tile, run); each writes its normalised partial O (fp32) and partial
@@ -80,6 +91,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     constexpr int BUF_BYTES = 2 * T_BYTES;           // K tile + V tile
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_BYTES];
+    __shared__ int redo_flag[4];   // per wave: a row left the fast path's range
 
     // wave index through readfirstlane: everything derived from it (LDS
     // addresses, the per-wave causal limits) stays in scalar registers
@@ -111,6 +123,9 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
     const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
     const int offl = off - (MASK == kMaskWindow ? p.wl : 0);
+    // the fast softmax path (kFastSumLimit); split-KV runs, bound by HBM,
+    // keep the per-tile maximum
+    constexpr bool kFast = !SPLIT;
     const bf16* Qh = (const bf16*)p.q + sg.q_row0 * D;
     const bf16* Kh = (const bf16*)p.k + sg.k_row0 * D;
     const bf16* Vh = (const bf16*)p.v + sg.k_row0 * D;
@@ -154,6 +169,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
 
     int b0 = 0;               // LDS buffer of the current item's first key tile
     bool prefetched = false;  // its Q and first key tile were issued by the previous item
+    bool careful = false;     // recomputation of an item: row maximum on every tile
     for (int it = 0; it < n_items; ++it) {
     const int qt = it == 0 ? nqt - 1 - slot : slot;
     const int q0 = qt * BR;
@@ -175,6 +191,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     float m_run = -INFINITY;   // running max of scale*log2e*S for this lane's query
     float l_run = 0.f;         // partial running sum over this lane's keys
     float nbase = 0.f;         // -m_run, or 0 while the row has seen no key (every term is then 0)
+    bool have_base = false;    // every row of the wave has a base (wave-uniform)
 
     // Q into the idle buffer b0^1 (issued after the previous item's loop
     // when that item prefetched this one's first key tile into b0)
@@ -251,6 +268,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
             // kRescaleSlack; otherwise P = 2^(s - m_run) <= 2^kRescaleSlack and
             // nothing is rescaled.  Exact after the final O / l ("FlashAttention
             // 1～4 全解汇总", FlashAttention-4 conditional softmax rescaling).
+            if (!kFast || careful || !have_base) {
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -272,6 +290,9 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
                     for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
                 m_run = m_new;
                 nbase = (m_run == -INFINITY) ? 0.f : -m_run;
+            }
+            // a row with no visible key so far keeps the maximum path
+            have_base = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0;
             }
             // ---- P and O^T += V^T P^T, one 16-key block at a time ----
             // A block's P is packed right before its P.V MFMAs, so the
@@ -322,6 +343,24 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         if (has_next) vmem_wait_all();   // this wave's copies of the next tile landed
         tile_barrier();
     }
+    if (kFast && !careful && ntiles > 0) {
+        // did any wave of the workgroup leave the fast path's range?  Then
+        // run this item again, from its Q tile, with the per-tile maximum;
+        // both LDS buffers are reloaded (the recomputation's last tile
+        // fetches the next item's first tile again).
+        // l_run only grows (a sum of terms >= 0; inf and NaN persist), so its
+        // final value is checked once, after the last tile
+        const bool bad = __builtin_amdgcn_ballot_w64(!(l_run <= kFastSumLimit)) != 0;
+        if (lane == 0) redo_flag[wave] = bad ? 1 : 0;
+        tile_barrier();
+        if ((redo_flag[0] | redo_flag[1] | redo_flag[2] | redo_flag[3]) != 0) {
+            careful = true;
+            prefetched = false;
+            --it;
+            continue;
+        }
+    }
+    careful = false;
 
     // The next item's first key tile is already in LDS (buffer b0 below);
     // the other buffer is idle since the loop's last barrier.  At d = 128 the

@@ -1,0 +1,170 @@
+"""GPU parity of the forward's fixed-base softmax path (MI355X only).
+
+The bf16 forward takes each row's scaling base from the first key tile a wave
+sees, then skips the row maximum on later tiles; a row whose running sum
+leaves [0, 2^64] (its later logits far above the first tile's maximum) makes
+the workgroup recompute its query tile with the per-tile maximum.  Inputs
+from N(0, 1) never leave that range, so these cases plant one key per chosen
+row whose logit exceeds every logit of the first key tile by a set margin
+(in log2 units: scale * log2(e) * (q.k_jump - max_j q.k_j)):
+
+  * ~20    : P up to 2^20, the fixed base holds (no recomputation);
+  * ~80    : P finite but beyond 2^64 -> recomputation;
+  * ~200   : P overflows to +inf on the fixed base -> recomputation (without
+             it the row would come out inf / NaN).
+
+Each case compares whole heads with the fp64 oracle, both on the rows with a
+planted key and on every other row (the recomputed query tiles hold rows of
+both kinds), for plain, causal (paired and unpaired), local-window and
+variable-length launches.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_20_amd as fa
+import workloads as wl
+from oracle import attention_forward, varlen_forward
+from parity import check_forward, to64
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def amplitude(margin, d):
+    """A with scale*log2e*(A^2 - 3A) ~= margin (bf16-exact integer): the
+    planted logit is A*A, the first tile's largest about 3*A."""
+    c = LOG2E / math.sqrt(d)
+    a = (3.0 + math.sqrt(9.0 + 4.0 * margin / c)) / 2.0
+    return float(round(a))
+
+
+def plant(q, k, rows, margin, d, window_left=None):
+    """Row r gets q_r = A e_0 and its key j_r = r (the diagonal, visible under
+    causal and local windows) gets k_j[0] = A, so S_rj = A^2 while the first
+    key tile's logits stay near A * N(0, 1).  In place on [B, H, N, d] bf16."""
+    A = amplitude(margin, d)
+    for (b, h, r) in rows:
+        q[b, h, r, :] = 0
+        q[b, h, r, 0] = A
+        k[b, h, r, 0] = A
+    return A
+
+
+def planted_rows(B, H, N, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    out = []
+    for _ in range(n):
+        b = int(torch.randint(B, (1,), generator=g))
+        h = int(torch.randint(H, (1,), generator=g))
+        r = int(torch.randint(64, N, (1,), generator=g))   # past the first key tile
+        out.append((b, h, r))
+    return out
+
+
+def check_heads(q, k, v, o, lse, scale, causal, heads, what, window=None):
+    for (b, h) in heads:
+        o_ref, lse_ref = attention_forward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), scale,
+                                           causal, window=window)
+        check_forward(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, "bf16", f"{what} head {(b, h)}")
+
+
+CASES = [
+    # B, H, N, d, causal, margin
+    (1, 4, 1000, 128, True, 20),
+    (1, 4, 1000, 128, True, 80),
+    (1, 4, 1000, 128, True, 200),
+    (1, 4, 777, 128, False, 200),
+    (2, 3, 640, 64, True, 80),
+    (2, 3, 640, 64, False, 200),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_planted_logit_jumps(case):
+    B, H, N, d, causal, margin = case
+    banner(f"fwd planted jump {case}")
+    q, k, v = wl.make_inputs(B, H, N, N, d, "bf16", seed=4400 + N + d + margin)
+    rows = planted_rows(B, H, N, 6, seed=N + margin)
+    A = plant(q, k, rows, margin, d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_forward(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all(), f"{case}: non-finite output"
+    heads = sorted({(b, h) for (b, h, _) in rows})
+    check_heads(q, k, v, o, lse, scale, causal, heads, f"{case} A={A}")
+    # a head with no planted key stays on the fixed base
+    clean = [(b, h) for b in range(B) for h in range(H) if (b, h) not in heads][:1]
+    check_heads(q, k, v, o, lse, scale, causal, clean, f"{case} clean")
+
+
+def test_planted_jump_in_paired_workgroups():
+    """d = 64 causal over >= 2048 query tiles: a workgroup runs tile n-1-j,
+    then j; a recomputation of the first must leave the second (whose first
+    key tile was prefetched) correct."""
+    B, H, N, d = 1, 256, 1024, 64
+    assert B * H * ((N + 127) // 128) >= 2048
+    banner(f"fwd planted jump paired B{B} H{H} N{N} d{d}")
+    q, k, v = wl.make_inputs(B, H, N, N, d, "bf16", seed=4501)
+    g = torch.Generator().manual_seed(4502)
+    heads = [(0, int(h)) for h in torch.randperm(H, generator=g)[:4].tolist()]
+    rows = []
+    for i, (b, h) in enumerate(heads):
+        rows.append((b, h, N - 1 - 37 * i))        # last query tile (a workgroup's first item)
+        rows.append((b, h, 200 + 129 * i))         # a middle tile
+    A = plant(q, k, rows, 200, d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_forward(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    check_heads(q, k, v, o, lse, scale, True, heads + [(0, 0)], f"paired A={A}")
+
+
+def test_planted_jump_under_local_window():
+    B, H, N, d = 1, 2, 900, 128
+    window = (300, 0)
+    banner(f"fwd planted jump window {window}")
+    q, k, v = wl.make_inputs(B, H, N, N, d, "bf16", seed=4601)
+    rows = [(0, 0, 500), (0, 1, 899), (0, 1, 140)]
+    plant(q, k, rows, 200, d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_forward(q.cuda(), k.cuda(), v.cuda(), scale=scale, window=window)
+    torch.cuda.synchronize()
+    check_heads(q, k, v, o.cpu(), lse.cpu(), scale, False, [(0, 0), (0, 1)], "window",
+                window=window)
+
+
+def test_planted_jump_in_varlen_batch():
+    H, d = 2, 128
+    lens = [300, 77, 520]
+    banner(f"fwd planted jump varlen {lens}")
+    total = sum(lens)
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    g = torch.Generator().manual_seed(4701)
+    q = torch.randn(H, total, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(H, total, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(H, total, d, generator=g).to(torch.bfloat16)
+    A = amplitude(200, d)
+    for (h, t) in [(0, 0 + 250), (1, cu[2] + 400), (1, cu[2] + 100)]:
+        q[h, t, :] = 0
+        q[h, t, 0] = A
+        k[h, t, 0] = A
+    cu_t = torch.tensor(cu, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_forward_varlen(q.cuda(), k.cuda(), v.cuda(), cu_t.cuda(), cu_t.cuda(),
+                                         max(lens), max(lens), scale=scale, causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = varlen_forward(to64(q), to64(k), to64(v), np.array(cu), np.array(cu), scale,
+                                    causal=True)
+    check_forward(to64(o), to64(lse), o_ref, lse_ref, "bf16", "varlen planted")
