@@ -228,8 +228,24 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
                     dp[qb] = mfma_bf16(tile_read_row<D>(dos, qb * 32, kk, lane), vreg[kk], dp[qb]);
                 }
             // ---- P = 2^(S*scale*log2e - LSE2), dS = P * (dP - D) ----
+            // ---- mask: only steps that straddle a bound or the tail ----
             const bool need_mask = (q0 + BQ > Nq) || (kRight && q0 + offr < kw + 31) ||
                                    (kLeft && q0 + BQ - 1 + offl > kw);
+            if (need_mask) {
+                // item 4g+e of block qb is query q0 + 4*hg + o, o = qb*32 + g*8 + e:
+                // visible iff lo <= o <= hi (q < Nq, kj <= q + offr, kj >= q + offl)
+                const int qb0 = q0 + 4 * hg;
+                const int lo = kRight ? kj - offr - qb0 : -(1 << 30);
+                int hi = Nq - 1 - qb0;
+                if (kLeft) hi = min(hi, kj - offl - qb0);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int o = qb * 32 + (i >> 2) * 8 + (i & 3);
+                        if (o < lo || o > hi) s[qb][i] = -INFINITY;
+                    }
+            }
             u32x4 pw[NQC], dsw[NQC];
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
@@ -241,12 +257,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
                     const f32x4 dd = *(const f32x4*)(dds + ql);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float sv = s[qb][4 * g + e];
-                        if (need_mask) {
-                            const int q = q0 + ql + e;
-                            const bool vis = q < Nq && (!kRight || kj <= q + offr) && (!kLeft || kj >= q + offl);
-                            if (!vis) sv = -INFINITY;
-                        }
+                        const float sv = s[qb][4 * g + e];
                         const float pe = exp2_hw(fmaf(sv, p.scale_log2, -l2[e]));
                         pv[4 * g + e] = pe;
                         dsv[4 * g + e] = pe * (dp[qb][4 * g + e] - dd[e]);
@@ -417,20 +428,31 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
                     dp[kb] = mfma_bf16(tile_read_row<D>(vbuf, kb * 32, kk, lane), doreg[kk], dp[kb]);
                 }
             // ---- dS^T = P * (dP - D), P = 2^(S*scale*log2e - LSE2) ----
+            // ---- mask: only tiles that straddle a bound or the tail ----
             const bool need_mask = (k0 + BC > Nk) || (kRight && k0 + BC - 1 > qw + offr) ||
                                    (kLeft && k0 < qw + 31 + offl);
+            if (need_mask) {
+                // item i of block kb is key k0 + 4*hg + o, o = kb*32 + (i/4)*8 + i%4:
+                // visible iff lo <= o <= hi (key < Nk, key <= qi + offr, key >= qi + offl)
+                const int kb0 = k0 + 4 * hg;
+                int hi = Nk - 1 - kb0;
+                if (kRight) hi = min(hi, qi + offr - kb0);
+                const int lo = kLeft ? qi + offl - kb0 : -(1 << 30);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
+                        if (o < lo || o > hi) s[kb][i] = -INFINITY;
+                    }
+            }
             u32x4 dsw[NKC];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 float dsv[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    float sv = s[kb][i];
-                    if (need_mask) {
-                        const int key = k0 + kb * 32 + (i >> 2) * 8 + 4 * hg + (i & 3);
-                        const bool vis = key < Nk && (!kRight || key <= qi + offr) && (!kLeft || key >= qi + offl);
-                        if (!vis) sv = -INFINITY;
-                    }
+                    const float sv = s[kb][i];
                     const float pe = exp2_hw(fmaf(sv, p.scale_log2, -l2));
                     dsv[i] = pe * (dp[kb][i] - dd);
                 }
