@@ -227,6 +227,20 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
                     s[qb] = mfma_bf16(tile_read_row<D>(qs, qb * 32, kk, lane), kreg[kk], s[qb]);
                     dp[qb] = mfma_bf16(tile_read_row<D>(dos, qb * 32, kk, lane), vreg[kk], dp[qb]);
                 }
+            // At d = 128 the operand reads run four ahead of the MFMAs here and
+            // two per MFMA in the products below (+4.9% on the Llama-shaped
+            // backward); at d = 64 the compiler's own order measured 1.8% faster.
+            if constexpr (D == 128) {
+                constexpr int nm = 2 * NKK * NQB;
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < nm - 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
             // ---- P = 2^(S*scale*log2e - LSE2), dS = P * (dP - D) ----
             // ---- mask: only steps that straddle a bound or the tail ----
             const bool need_mask = (q0 + BQ > Nq) || (kRight && q0 + offr < kw + 31) ||
@@ -275,6 +289,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
                 for (int db = 0; db < NDB; ++db) {
                     dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qc * 16, db * 32, lane), pb, dvacc[db]);
                     dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qc * 16, db * 32, lane), sb, dkacc[db]);
+                }
+            }
+            if constexpr (D == 128) {   // two transposed reads per MFMA
+                constexpr int nm = 2 * NQC * NDB;
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+                for (int i = 0; i < nm; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                    if (i < nm - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
                 }
             }
         }
@@ -427,6 +450,18 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
                     s[kb] = mfma_bf16(tile_read_row<D>(kbuf, kb * 32, kk, lane), qreg[kk], s[kb]);
                     dp[kb] = mfma_bf16(tile_read_row<D>(vbuf, kb * 32, kk, lane), doreg[kk], dp[kb]);
                 }
+            // operand reads four ahead of the MFMAs at d = 128, as in dK/dV
+            if constexpr (D == 128) {
+                constexpr int nm = 2 * NKK * NKB;
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < nm - 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
             // ---- dS^T = P * (dP - D), P = 2^(S*scale*log2e - LSE2) ----
             // ---- mask: only tiles that straddle a bound or the tail ----
             const bool need_mask = (k0 + BC > Nk) || (kRight && k0 + BC - 1 > qw + offr) ||
@@ -465,6 +500,15 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
                     dqacc[db] = mfma_bf16(tile_read_tr<D>(kbuf, kc * 16, db * 32, lane), sb, dqacc[db]);
+            }
+            if constexpr (D == 128) {   // two transposed reads per MFMA
+                constexpr int nm = NKC * NDB;
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+                for (int i = 0; i < nm; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                    if (i < nm - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+                }
             }
         }
 
