@@ -69,10 +69,11 @@ constexpr float kFastSumLimit = 0x1p64f;
 // LSE (log2 units) to p.o_part / p.lse_part, and fwd_combine_kernel merges
 // them.  Without SPLIT the workgroup owns whole query tiles.
 // Waves per SIMD the register budget must allow: 2 at d = 128 (LDS holds
-// two workgroups per CU), 4 at d = 64 (32 KiB of LDS per workgroup, so four
-// workgroups per CU fit if the kernel stays within 128 VGPRs).
+// two workgroups per CU), 3 at d = 64 (32 KiB of LDS per workgroup; 2, 3
+// and 4 measured the same without the output staging, and 3 leaves the
+// staging its registers).
 template <int D>
-constexpr int fwd_waves_per_simd() { return D == 64 ? 4 : 2; }
+constexpr int fwd_waves_per_simd() { return D == 64 ? 3 : 2; }
 
 // MASK: kMaskNone, kMaskCausal (key j visible to query i iff j <= i + off,
 // off = Nk - Nq) or kMaskWindow (iff i + off - wl <= j <= i + off + wr, the
@@ -363,12 +364,13 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     careful = false;
 
     // The next item's first key tile is already in LDS (buffer b0 below);
-    // the other buffer is idle since the loop's last barrier.  At d = 128 the
-    // epilogue stages O there first; otherwise it takes the next item's Q
+    // the other buffer is idle since the loop's last barrier.  The epilogue
+    // stages O there first, except in the causal d = 64 kernel (the one whose
+    // launches pair query tiles): there the buffer takes the next item's Q
     // tile right away, while this item's epilogue runs.
     prefetched = next_ntiles > 0 && ntiles > 0;
     b0 = (b0 + ntiles) & 1;
-    constexpr bool kStageO = D == 128;
+    constexpr bool kStageO = D == 128 || MASK != kMaskCausal;
     if (!kStageO && prefetched) load_q(slot * BR, b0 ^ 1);
 
     // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l) ----
@@ -393,14 +395,16 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         }
         continue;
     }
-    // At d = 128, O goes through LDS so that HBM sees whole rows: a lane
-    // holds one query's d values in 8-byte pieces, so direct stores write 32
-    // scattered 16-byte pieces per instruction and stall on their data
-    // registers.  Each wave writes its 32 rows into its own part of the idle
-    // buffer (swizzled like the K/V tiles), reads them back row-contiguous
-    // and stores 16 bytes per lane; no other wave touches those rows.  (At
-    // d = 64 the staging costs more than it saves: its registers push the
-    // kernel past the 128 VGPRs of four waves per SIMD.)
+    // O goes through LDS so that HBM sees whole rows: a lane holds one
+    // query's d values in 8-byte pieces, so direct stores write scattered
+    // 16-byte pieces per instruction and stall on their data registers.
+    // Each wave writes its 32 rows into its own part of the idle buffer
+    // (swizzled like the K/V tiles), reads them back row-contiguous and
+    // stores 16 bytes per lane; no other wave touches those rows.  (Measured
+    // +1.5% at d = 128 and +3.7% on the non-causal d = 64 GPT-2 shape; on
+    // paired causal d = 64 launches direct stores, which let the next item's
+    // Q tile load during the epilogue, measured 2.9% faster.  Choosing per
+    // item at run time cost 11% there, so the choice is per kernel.)
     if constexpr (kStageO) {
         char* ost = smem + (b0 ^ 1) * BUF_BYTES + wave * 32 * (D * 2);
 #pragma unroll
