@@ -152,55 +152,59 @@ __device__ __forceinline__ void async_load_lds16(i32x4 rsrc, uint32_t lds_addr, 
         : "memory");
 }
 
-// Eight such copies in one statement: 1 KiB each to consecutive LDS
-// addresses lds_addr, lds_addr + 1024, ... from per-lane offsets off[i] +
-// soff.  M0 is bound as an input (the compiler writes it); the statement
-// steps it by 1 KiB per copy and steps it back at the end, so M0 leaves the
-// statement holding the value the compiler put there.  The wait states are
-// paid once up front (5: VALU write of an SGPR operand before the
-// statement), then 1 after each M0 step.
+// Eight such copies in one statement: 1 KiB each to LDS addresses
+// lds_addr, lds_addr + STEP, ... (STEP >= 1024: consecutive pieces, or
+// pieces with padding between them) from per-lane offsets off[i] + soff.
+// M0 is bound as an input (the compiler writes it); the statement steps it
+// by STEP per copy and steps it back at the end, so M0 leaves the statement
+// holding the value the compiler put there.  The wait states are paid once
+// up front (5: VALU write of an SGPR operand before the statement), then 1
+// after each M0 step.
+template <uint32_t STEP = 1024>
 __device__ __forceinline__ void async_load_lds16_x8(i32x4 rsrc, uint32_t lds_addr, const uint32_t (&off)[8],
                                                     uint32_t soff) {
     asm volatile(
         "s_nop 4\n\t"
         "buffer_load_dwordx4 %0, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %1, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %2, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %3, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %4, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %5, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %6, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %7, %8, %9 offen lds\n\t"
-        "s_sub_u32 m0, m0, 0x1c00"
+        "s_sub_u32 m0, m0, %12"
         :
         : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "v"(off[5]), "v"(off[6]),
-          "v"(off[7]), "s"(rsrc), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+          "v"(off[7]), "s"(rsrc), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)),
+          "i"(STEP), "i"(7 * STEP)
         : "memory", "scc");
 }
 
 // The same for four copies.
+template <uint32_t STEP = 1024>
 __device__ __forceinline__ void async_load_lds16_x4(i32x4 rsrc, uint32_t lds_addr, const uint32_t (&off)[4],
                                                     uint32_t soff) {
     asm volatile(
         "s_nop 4\n\t"
         "buffer_load_dwordx4 %0, %4, %5 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %7\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %1, %4, %5 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %7\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %2, %4, %5 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+        "s_add_u32 m0, m0, %7\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %3, %4, %5 offen lds\n\t"
-        "s_sub_u32 m0, m0, 0xc00"
+        "s_sub_u32 m0, m0, %8"
         :
         : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(rsrc), "s"(soff),
-          "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+          "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)), "i"(STEP), "i"(3 * STEP)
         : "memory", "scc");
 }
 
@@ -351,6 +355,98 @@ struct TileCopy {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) async_load_lds16(rsrc, dst + lds_off + i * 1024, goff[i], soff);
         }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// LDS tiles of 128-wide bf16 rows with immediate operand offsets (the d = 128
+// forward kernel).  A tile of R rows is R/4 pieces of 1 KiB; piece p holds
+// rows p, p + R/4, p + 2R/4, p + 3R/4, each as 256 contiguous bytes, and the
+// pieces lie PS bytes apart:
+//   offset(row, chunk) = (row % (R/4)) * PS + 256 * (row / (R/4)) + 16 * chunk.
+// Then
+//   * one asynchronous copy (64 lanes x 16 bytes to consecutive LDS
+//     addresses) fills one piece, and each 16-lane group of it reads one
+//     whole 256-byte row from HBM;
+//   * the MFMA A-operand row read (lane = row r0 + l%32, chunk 2kk + l/32)
+//     and the transposed read (tile_read_tr's lanes) are a per-lane base
+//     plus an offset that depends only on the k-step and column block, so
+//     every operand address in a loop is base register + immediate;
+//   * with PS = kLinPieceK = 1040 the row reads of 16 consecutive rows hit
+//     16 distinct 16-byte bank groups (consecutive rows are consecutive
+//     pieces, 1040 = 65 * 16), and with PS = kLinPieceV = 1088 each 32-lane
+//     half of a transposed read covers the 64 banks once (1088 = 136 * 8).
+// K and the query tile use the first stride, V the second.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kLinPieceK = 1040, kLinPieceV = 1088;
+
+template <int ROWS, uint32_t PS>
+constexpr int lin_tile_bytes() {
+    static_assert(ROWS % 4 == 0, "whole pieces");
+    return ROWS / 4 * (int)PS;
+}
+
+// Byte offset of logical chunk `chunk` (16 bytes) of row `row`.
+template <int ROWS, uint32_t PS>
+__device__ __forceinline__ uint32_t lin_offset(uint32_t row, uint32_t chunk) {
+    constexpr uint32_t NP = ROWS / 4;
+    return (row % NP) * PS + 256 * (row / NP) + 16 * chunk;
+}
+
+// Per-lane base of the row read: lin_offset(l%32, l/32).
+template <int ROWS, uint32_t PS>
+__device__ __forceinline__ uint32_t lin_row_base(int lane) {
+    return lin_offset<ROWS, PS>(lane & 31, (lane >> 5) & 1);
+}
+
+// Row read (as tile_read_row): lane l gets the 8 columns 8*(2*kk + l/32) ..
+// +7 of row r0 + l%32; `p` = tile + lin_row_base(lane), r0 a multiple of 32.
+template <int ROWS>
+__device__ __forceinline__ bf16x8 lin_read_row(const char* p, uint32_t r0, int kk) {
+    return *(const bf16x8*)(p + 256 * (r0 / (ROWS / 4)) + 32 * kk);
+}
+
+// Per-lane base of the transposed read on a 64-row tile: the address
+// tile_read_tr's lane reads for r0 = c0 = 0 (row 4*(l/32) + (l%16)/4,
+// column 16*((l/16)%2) + 4*(l%4), 8 bytes).
+template <uint32_t PS>
+__device__ __forceinline__ uint32_t lin_tr_base(int lane) {
+    const uint32_t gi = lane & 15, hg = (lane >> 5) & 1, g16 = (lane >> 4) & 1;
+    const uint32_t col = 16 * g16 + 4 * (gi & 3);
+    return lin_offset<64, PS>(4 * hg + (gi >> 2), col >> 3) + (col & 4) * 2;
+}
+
+// Transposed read (as tile_read_tr) on a 64-row tile: the A operand whose
+// lane l holds column c0 + l%32 at rows r0 + 4g + {0..3} and r0 + 8 + 4g +
+// {0..3}, g = l/32; `p` = tile + lin_tr_base(lane), r0 a multiple of 16, c0
+// of 32.
+template <uint32_t PS>
+__device__ __forceinline__ bf16x8 lin_read_tr(const char* p, uint32_t r0, uint32_t c0) {
+    const char* q = p + 256 * (r0 / 16) + 2 * c0;
+    return concat8(lds_read_tr16(q), lds_read_tr16(q + 8 * PS));
+}
+
+// Asynchronous copy of ROWS x 128 bf16 rows into such a tile by WAVES waves
+// (the TileCopy interface): wave w fills pieces w*LOADS .. +LOADS-1.
+template <int ROWS, int WAVES, uint32_t PS>
+struct LinTileCopy {
+    static constexpr int NP = ROWS / 4;
+    static constexpr int LOADS = NP / WAVES;
+    static_assert(NP % WAVES == 0 && (LOADS == 4 || LOADS == 8), "whole pieces, 4 or 8 per wave");
+    uint32_t goff[LOADS];
+    uint32_t lds_off;
+    __device__ __forceinline__ LinTileCopy(int wave, int lane) {
+        lds_off = (uint32_t)(wave * LOADS) * PS;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const uint32_t row = (uint32_t)(wave * LOADS + i) + NP * (uint32_t)(lane >> 4);
+            goff[i] = row * 256 + 16 * (uint32_t)(lane & 15);
+        }
+    }
+    __device__ __forceinline__ void issue(const i32x4& rsrc, int row0, uint32_t dst) const {
+        const uint32_t soff = (uint32_t)row0 * 256;
+        if constexpr (LOADS == 8) async_load_lds16_x8<PS>(rsrc, dst + lds_off, goff, soff);
+        else async_load_lds16_x4<PS>(rsrc, dst + lds_off, goff, soff);
     }
 };
 

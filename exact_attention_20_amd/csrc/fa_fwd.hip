@@ -88,8 +88,16 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     constexpr int NKB = BC / 32;       // 32-key blocks per tile
     constexpr int NDB = D / 32;        // 32-row blocks of O^T
     constexpr int NKC = BC / 16;       // 16-key k-steps for O^T += V^T P^T
-    constexpr int T_BYTES = BC * D * 2;              // one K or V tile
-    constexpr int BUF_BYTES = 2 * T_BYTES;           // K tile + V tile
+    // d = 128 uses the linear-offset tiles (lin_offset: every operand read
+    // is one base register plus an immediate), d = 64 the swizzled ones
+    constexpr bool kLin = D == 128;
+    constexpr uint32_t PK = kLinPieceK, PV = kLinPieceV;
+    constexpr int K_BYTES = kLin ? lin_tile_bytes<BC, PK>() : BC * D * 2;   // one K tile
+    constexpr int V_BYTES = kLin ? lin_tile_bytes<BC, PV>() : BC * D * 2;   // one V tile
+    constexpr int BUF_BYTES = K_BYTES + V_BYTES;                            // K tile + V tile
+    using KCopy = std::conditional_t<kLin, LinTileCopy<BC, 4, PK>, TileCopy<D, BC, 4>>;
+    using VCopy = std::conditional_t<kLin, LinTileCopy<BC, 4, PV>, TileCopy<D, BC, 4>>;
+    using QCopy = std::conditional_t<kLin, LinTileCopy<BR, 4, PK>, TileCopy<D, BR, 4>>;
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_BYTES];
     __shared__ int redo_flag[4];   // per wave: a row left the fast path's range
@@ -138,13 +146,14 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // of tile t+1 before the first V read of tile t, which puts a full HBM /
     // L2 round trip inside every tile.  Completion is awaited explicitly at
     // the end-of-tile barrier instead.
-    const TileCopy<D, BC, 4> copier(wave, lane);
+    const KCopy kcopier(wave, lane);
+    const VCopy vcopier(wave, lane);
     const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
     const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
     const uint32_t smem_lds = lds_address(smem);
     auto load_tile = [&](int k0, int buf) {
-        copier.issue(rk_w, k0, smem_lds + buf * BUF_BYTES);
-        copier.issue(rv_w, k0, smem_lds + buf * BUF_BYTES + T_BYTES);
+        kcopier.issue(rk_w, k0, smem_lds + buf * BUF_BYTES);
+        vcopier.issue(rv_w, k0, smem_lds + buf * BUF_BYTES + K_BYTES);
     };
 
     // Q takes the same route: the BR x D query tile (exactly one K + V
@@ -154,8 +163,12 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // analysis never sees a load in flight inside the key loop; there the
     // hardware counter also counts the copies of the next key tile, and any
     // wait it placed would stall every tile on them.
-    static_assert(BR * D * 2 == BUF_BYTES, "a query tile fills one K + V buffer");
-    const TileCopy<D, BR, 4> qcopier(wave, lane);
+    static_assert((kLin ? lin_tile_bytes<BR, PK>() : BR * D * 2) <= BUF_BYTES, "a query tile fits one K + V buffer");
+    const QCopy qcopier(wave, lane);
+    // per-lane bases of the immediate-offset operand reads
+    const uint32_t kbase = kLin ? lin_row_base<BC, PK>(lane) : 0u;
+    const uint32_t qbase = kLin ? lin_row_base<BR, PK>(lane) : 0u;
+    const uint32_t trbase = kLin ? lin_tr_base<PV>(lane) : 0u;
     const i32x4 rq_w = make_rsrc_words(Qh, (uint32_t)Nq * D * 2);
     auto load_q = [&](int q0_, int buf) { qcopier.issue(rq_w, q0_, smem_lds + buf * BUF_BYTES); };
     bf16x8 qreg[NKK];
@@ -205,7 +218,8 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     {
         const char* qbuf = smem + (b0 ^ 1) * BUF_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = tile_read_row<D>(qbuf, wave * 32, kk, lane);
+        for (int kk = 0; kk < NKK; ++kk)
+            qreg[kk] = kLin ? lin_read_row<BR>(qbuf + qbase, wave * 32, kk) : tile_read_row<D>(qbuf, wave * 32, kk, lane);
     }
     tile_barrier();   // every wave holds its Q rows before b0^1 takes the next key tile
 
@@ -213,7 +227,9 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         const int k0 = t * BC;
         const int buf = (b0 + t - t_lo) & 1;
         const char* kbuf = smem + buf * BUF_BYTES;
-        const char* vbuf = kbuf + T_BYTES;
+        const char* vbuf = kbuf + K_BYTES;
+        const char* kread = kbuf + kbase;    // d = 128 tiles: operand = base + immediate
+        const char* vread = vbuf + trbase;
         // the other buffer takes the next key tile, or the next item's first
         const bool has_next = t + 1 < t_hi || next_ntiles > 0;
         if (t + 1 < t_hi) load_tile(k0 + BC, buf ^ 1);
@@ -228,7 +244,8 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
             for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    s[kb] = mfma_bf16(tile_read_row<D>(kbuf, kb * 32, kk, lane), qreg[kk], s[kb]);
+                    s[kb] = mfma_bf16(kLin ? lin_read_row<BC>(kread, kb * 32, kk) : tile_read_row<D>(kbuf, kb * 32, kk, lane),
+                                      qreg[kk], s[kb]);
                 }
             }
             // K-operand reads run 4 ahead of the MFMAs: 4 reads, then alternate
@@ -317,7 +334,8 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    oacc[db] = mfma_bf16(tile_read_tr<D>(vbuf, kc * 16, db * 32, lane), pb, oacc[db]);
+                    oacc[db] = mfma_bf16(kLin ? lin_read_tr<PV>(vread, kc * 16, db * 32) : tile_read_tr<D>(vbuf, kc * 16, db * 32, lane),
+                                         pb, oacc[db]);
             }
             l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
             // Issue order: the first block's 28 VALU instructions (8 FMA, 8
@@ -405,7 +423,29 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // paired causal d = 64 launches direct stores, which let the next item's
     // Q tile load during the epilogue, measured 2.9% faster.  Choosing per
     // item at run time cost 11% there, so the choice is per kernel.)
-    if constexpr (kStageO) {
+    if constexpr (kStageO && kLin) {
+        // the query-sized region in the query tile's layout: the wave's row
+        // r (of 32) is row 32*wave + r, i.e. piece r at offset 256*wave; read
+        // back four rows per pass (16 lanes a row), stored as whole rows
+        char* obuf = smem + (b0 ^ 1) * BUF_BYTES;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+                w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                *(u32x2*)(obuf + lin_offset<BR, PK>(wave * 32 + l32, db * 4 + g) + hg * 8) = w;
+            }
+        bf16* Ow = (bf16*)p.o + sg.q_row0 * D + (size_t)qw * D;
+        const int rr = lane >> 4, cc = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + rr;
+            const u32x4 x = *(const u32x4*)(obuf + lin_offset<BR, PK>(wave * 32 + r, cc));
+            if (qw + r < Nq) *(u32x4*)(Ow + (size_t)r * D + cc * 8) = x;
+        }
+    } else if constexpr (kStageO) {
         char* ost = smem + (b0 ^ 1) * BUF_BYTES + wave * 32 * (D * 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
