@@ -35,9 +35,11 @@ def test_copy_piece_is_one_dma_and_whole_rows():
             for lane in range(64):
                 row, chunk = p + (rows // 4) * (lane >> 4), lane & 15
                 assert off(row, chunk, rows, ps) == p * ps + 16 * lane
-            # each 16-lane group reads one row's 256 contiguous bytes
+            # each 16-lane group reads one row's 256 contiguous bytes, in order
             for g in range(4):
-                assert len({p + (rows // 4) * g for _ in range(16)}) == 1
+                src = [(p + (rows // 4) * (lane >> 4), lane & 15) for lane in range(16 * g, 16 * g + 16)]
+                assert len({r for r, _ in src}) == 1
+                assert [c for _, c in src] == list(range(16))
 
 
 def test_row_read_base_plus_immediate_and_conflict_free():
