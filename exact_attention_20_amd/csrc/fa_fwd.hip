@@ -495,50 +495,75 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
 //   LSE = ln2 * (M + log2 sum_s w_s).
 // A row no run saw (every L_s = -inf) gets O = 0, LSE = -inf.
 // One workgroup of 256 threads per row: thread t owns 8 output columns
-// (chunk t % (D/8)) of the runs s = t / (D/8), + 256 / (D/8), ...; the
-// partial sums are then added across the run lanes through LDS.
+// (chunk t % (D/8)) of the runs s = t / (D/8), + 256 / (D/8), ...; it loads
+// four of its runs at a time and merges them with the same rescale against
+// its own running maximum, so a thread waits for memory once per four runs
+// (one round trip at the decode shape).  The threads' partial sums are then
+// rescaled to the block's maximum and added across the run lanes through
+// LDS.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdParams p) {
     constexpr int TPR = D / 8;          // 8-column chunks per row
     constexpr int J = 256 / TPR;        // run lanes
+    constexpr int U = 4;                // runs a thread loads at once
     __shared__ float red[J][D + 4];
     __shared__ float wred[4];
     const long rows = (long)p.BH * p.Nq;
     const long row = blockIdx.x;
     const int t = threadIdx.x, c = t % TPR, j = t / TPR;
     const int ns = p.n_splits;
-    // M = max over the runs: strided over all 256 threads, then reduced
-    float M = -INFINITY;
-    for (int s = t; s < ns; s += 256) M = fmaxf(M, p.lse_part[(size_t)s * rows + row]);
+    // Each thread merges its runs s = j, j + J, ... U at a time (all loads of
+    // a group in flight together) with the online rescale, keeping its own
+    // maximum Mt; the threads' results are then rescaled to the block's M.
+    float Mt = -INFINITY, wsum = 0.f;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int s0 = j; s0 < ns; s0 += U * J) {
+        float L[U];
+        f32x4 a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * J;
+            const bool ok = s < ns;
+            const size_t r = (size_t)(ok ? s : 0) * rows + row;
+            L[u] = ok ? p.lse_part[r] : -INFINITY;
+            const float* Op = p.o_part + r * D + c * 8;
+            a[u] = *(const f32x4*)Op;          // run 0's values when !ok: weight 0 below
+            b[u] = *(const f32x4*)(Op + 4);
+        }
+        float mc = Mt;
+#pragma unroll
+        for (int u = 0; u < U; ++u) mc = fmaxf(mc, L[u]);
+        if (mc == -INFINITY) continue;          // no run of this group (or before) saw a key
+        const float alpha = exp2_hw(Mt - mc);   // 0 while Mt = -inf
+        wsum *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+        Mt = mc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = L[u] == -INFINITY ? 0.f : exp2_hw(L[u] - Mt);
+            wsum += w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] = fmaf(w, a[u][e], acc[e]);
+                acc[4 + e] = fmaf(w, b[u][e], acc[4 + e]);
+            }
+        }
+    }
+    // M = max over the threads' maxima
+    float M = Mt;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     if ((t & 63) == 0) wred[t >> 6] = M;
     __syncthreads();
     M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-    float acc[8];
+    const float scale = Mt == -INFINITY ? 0.f : exp2_hw(Mt - M);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    float wsum = 0.f;
-    if (M != -INFINITY) {
-        for (int s = j; s < ns; s += J) {
-            const float L = p.lse_part[(size_t)s * rows + row];
-            if (L == -INFINITY) continue;
-            const float w = exp2_hw(L - M);
-            wsum += w;
-            const float* Op = p.o_part + ((size_t)s * rows + row) * D + c * 8;
-            const f32x4 a = *(const f32x4*)Op;
-            const f32x4 b = *(const f32x4*)(Op + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[e] = fmaf(w, a[e], acc[e]);
-                acc[4 + e] = fmaf(w, b[e], acc[4 + e]);
-            }
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[j][c * 8 + e] = acc[e];
-    if (c == 0) red[j][D] = wsum;
+    for (int e = 0; e < 8; ++e) red[j][c * 8 + e] = acc[e] * scale;
+    if (c == 0) red[j][D] = wsum * scale;
     __syncthreads();
     if (t < D) {
         float o = 0.f, ws = 0.f;
