@@ -36,6 +36,9 @@ CASES = [
     (1, 1, 16, 64, 64, False, 1),       # one run: no split
     (2, 2, 1, 33000, 128, False, 0),    # long decode, ragged last tile
     (1, 3, 130, 2000, 64, False, 1000), # more runs asked for than tiles exist
+    (1, 2, 1, 70, 128, True, 5),        # one query row: more runs than key tiles
+    (3, 2, 1, 2500, 64, True, 0),       # one query row, d = 64, automatic runs
+    (1, 1, 1, 200, 128, False, 1),      # one query row, one run
 ]
 
 
@@ -77,3 +80,30 @@ def test_decode_workload_sampled_heads():
         b, h = divmod(bh, w.H)
         o_ref, lse_ref = attention_forward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), w.scale, w.causal)
         check_forward(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, "bf16", f"{w.name} head {bh}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_large_logit_jump_and_agreement(d):
+    """Single query row: keys whose logits exceed the earlier ones by ~200
+    log2 units (each run's scaling base and the combine's rescale must
+    follow them), checked against the oracle; plus run-to-run determinism
+    and agreement with fa_fwd."""
+    banner(f"decode jump d={d}")
+    B, H, Nk = 1, 3, 3000
+    q, k, v = wl.make_inputs(B, H, 1, Nk, d, "bf16", seed=3500 + d)
+    A = 40.0 if d == 128 else 34.0
+    for h, j in ((0, 2999), (1, 1500), (2, 7)):
+        q[0, h, 0, :] = 0
+        q[0, h, 0, 0] = A
+        k[0, h, j, 0] = A
+    scale = 1.0 / np.sqrt(d)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o1, l1 = fa.attention_forward_splitkv(qd, kd, vd, scale=scale, causal=True, n_splits=6)
+    o2, l2 = fa.attention_forward_splitkv(qd, kd, vd, scale=scale, causal=True, n_splits=6)
+    o0, l0 = fa.attention_forward(qd, kd, vd, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, lse_ref = attention_forward(to64(q), to64(k), to64(v), scale, True)
+    check_forward(to64(o1), to64(l1), o_ref, lse_ref, "bf16", f"decode jump d={d}")
+    assert (o1.float() - o0.float()).abs().max().item() <= 2e-2
+    assert (l1 - l0).abs().max().item() <= 1e-3
