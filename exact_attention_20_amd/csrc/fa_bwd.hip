@@ -426,6 +426,17 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     }
     mark_loaded(l2);
     mark_loaded(dd);
+    // dP - D in the dP product itself: one more k-step whose A operand is 1
+    // in columns 0 and 1 for every key and whose B operand holds -D split
+    // into two bf16 parts (hi + lo = -D within 2^-16 relative), so the
+    // accumulator ends at dP - D and dS = P * acc needs no subtraction
+    u32x4 ones_w = zero_u32x4(), negd_w = zero_u32x4();
+    if (hg == 0) {
+        const float dh = bf16_lo(pack_bf16x2(-dd, 0.f));   // -D rounded to bf16
+        ones_w[0] = pack_bf16x2(1.f, 1.f);
+        negd_w[0] = pack_bf16x2(-dd, -dd - dh);
+    }
+    const bf16x8 ones_a = __builtin_bit_cast(bf16x8, ones_w), negd_b = __builtin_bit_cast(bf16x8, negd_w);
 
     for (int t = t_first; t < ntiles; ++t) {
         const int k0 = t * BC;
@@ -441,7 +452,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 s[kb] = zero16();
-                dp[kb] = zero16();
+                dp[kb] = mfma_bf16(ones_a, negd_b, zero16());   // -D in every item
             }
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
@@ -489,7 +500,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
                 for (int i = 0; i < 16; ++i) {
                     const float sv = s[kb][i];
                     const float pe = exp2_hw(fmaf(sv, p.scale_log2, -l2));
-                    dsv[i] = pe * (dp[kb][i] - dd);
+                    dsv[i] = pe * dp[kb][i];   // dp holds dP - D
                 }
                 pack_pairs(dsv, dsw[2 * kb], dsw[2 * kb + 1]);
             }
