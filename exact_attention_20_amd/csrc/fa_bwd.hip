@@ -5,59 +5,34 @@
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three launches on the caller's stream, no atomics (deterministic):
-//   1. prep : per query row, D = rowsum(dO * O) and LSE in log2 units
-//             (+inf for a row with no visible key, so its P is exactly 0).
-//   2. dK/dV: one workgroup per (batch*head, 128-key tile) walking the query
-//             tiles that can see it (the loop order of §5).  Each wave owns 32
-//             keys: K and V sit in registers, Q / dO tiles stream through LDS,
-//             dK and dV accumulate in registers for the whole walk.
-//   3. dQ   : one workgroup per (batch*head, 128-query tile) walking the key
+// Two launches on the caller's stream, no atomics (deterministic):
+//   1. dQ   : one workgroup per (batch*head, 128-query tile) walking the key
 //             tiles it can see, like the forward pass.  Each wave owns 32
 //             queries: Q and dO sit in registers, K / V tiles stream through
-//             LDS, dQ accumulates in registers.
-// S and dP are computed in both 2 and 3 (7 products instead of 5) in exchange
-// for no dQ atomics and no dS round trip through memory.
+//             LDS, dQ accumulates in registers.  It first computes its rows'
+//             D = rowsum(dO * O) and LSE in log2 units (+inf for a row with
+//             no visible key, so its P is exactly 0) and writes both to the
+//             workspace.
+//   2. dK/dV: one workgroup per (batch*head, 128-key tile) walking the query
+//             tiles that can see it (the loop order of §5), reading D and
+//             LSE2 from the workspace.  Each wave owns 32 keys: K and V sit in
+//             registers, Q / dO tiles stream through LDS, dK and dV
+//             accumulate in registers for the whole walk.
+// S and dP are computed in both (7 products instead of 5) in exchange for no
+// dQ atomics and no dS round trip through memory.
 //
 // Register formulation (32x32x16 bf16 MFMA, fp32 accumulate).  In each main
 // kernel the products over the head dimension (S, dP) take the streamed tile
 // as the A operand (ds_read_b128 rows) and the resident operand from
 // registers, so each lane ends up owning ONE row of the resident side (a key
-// in 2, a query in 3) with 16 of its partners per 32-block -- exactly the B
+// in dK/dV, a query in dQ) with 16 of its partners per 32-block -- exactly the B
 // operand layout of the products over the streamed side (dV^T += dO^T P and
-// dK^T += Q^T dS in 2, dQ^T += K^T dS^T in 3), whose A operands are
+// dK^T += Q^T dS, dQ^T += K^T dS^T), whose A operands are
 // transposed reads (ds_read_b64_tr_b16) of the same LDS tiles.
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
-
-// ---------------------------------------------------------------------------
-// 1. D_i = sum_d dO_i * O_i (fp32); LSE_i * log2(e), or +inf for an empty row.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256) bwd_prep_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
-                                                       const float* __restrict__ lse, float* __restrict__ dvec,
-                                                       float* __restrict__ lse2, long rows) {
-    constexpr int TPR = D / 8;      // threads per row, 8 bf16 each
-    constexpr int RPB = 256 / TPR;  // rows per block
-    const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
-    const int c = threadIdx.x % TPR;
-    float acc = 0.f;
-    if (row < rows) {
-        const u32x4 a = ldg128(O + row * D + c * 8);
-        const u32x4 b = ldg128(dO + row * D + c * 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(b[i]) + bf16_hi(a[i]) * bf16_hi(b[i]);
-    }
-#pragma unroll
-    for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (row < rows && c == 0) {
-        dvec[row] = acc;
-        const float L = lse[row];
-        lse2[row] = L == -INFINITY ? INFINITY : L * kLog2e;
-    }
-}
 
 // Pack the P (or dS) values of a 32x32 accumulator into the bf16 B operands
 // of two 16-wide k-steps: item i = 4g + e of the accumulator (partner
@@ -374,6 +349,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, (uint32_t)Nq * D * 2);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dOh, (uint32_t)Nq * D * 2);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const bf16*)p.o + sg.q_row0 * D, (uint32_t)Nq * D * 2);
     const TileCopy<D, BC, 4> copier(wave, lane);
     const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
     const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
@@ -391,19 +367,18 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     const int kend_w = kRight ? min(Nk, qw + 32 + offr) : Nk;
     const int kbeg_w = kLeft ? qw + offl : 0;
 
-    // this lane's query: Q and dO as B operands, its LSE2 and D
+    // this lane's query: Q and dO as B operands, and the same columns of O
+    // (for D = rowsum(dO * O)), its LSE
     bf16x8 qreg[NKK], doreg[NKK];
+    u32x4 oreg[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         const uint32_t o = (uint32_t)qi * D * 2 + (16 * kk + 8 * hg) * 2;
         qreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rq, o, 0));
         doreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rdo, o, 0));
+        oreg[kk] = buf_load128(ro, o, 0);
     }
-    float l2 = INFINITY, dd = 0.f;             // rows past Nq: P = 0
-    if (qi < Nq) {
-        l2 = p.lse2[sg.q_row0 + qi];
-        dd = p.dvec[sg.q_row0 + qi];
-    }
+    const float lse_i = qi < Nq ? p.lse[sg.q_row0 + qi] : -INFINITY;
 
     auto load_tile = [&](int k0, int buf) {
         copier.issue(rk_w, k0, smem_lds + buf * BUF_BYTES);
@@ -423,9 +398,27 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     for (int kk = 0; kk < NKK; ++kk) {
         mark_loaded(qreg[kk]);
         mark_loaded(doreg[kk]);
+        mark_loaded(oreg[kk]);
     }
-    mark_loaded(l2);
-    mark_loaded(dd);
+    mark_loaded(lse_i);
+    // D = rowsum(dO * O) in fp32 (this lane's half of the columns, then the
+    // partner lane's) and LSE * log2(e) (+inf for a row with no visible key,
+    // so its P is exactly 0).  The dK/dV kernel, launched after this one,
+    // reads both from the workspace.
+    float dd = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 dw = __builtin_bit_cast(u32x4, doreg[kk]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dd += bf16_lo(dw[i]) * bf16_lo(oreg[kk][i]) + bf16_hi(dw[i]) * bf16_hi(oreg[kk][i]);
+    }
+    dd = xhalf_sum(dd);
+    // rows past Nq: P = 0
+    const float l2 = qi < Nq ? (lse_i == -INFINITY ? INFINITY : lse_i * kLog2e) : INFINITY;
+    if (qi < Nq && hg == 0) {
+        p.lse2[sg.q_row0 + qi] = l2;
+        p.dvec[sg.q_row0 + qi] = dd;
+    }
     // dP - D in the dP product itself: one more k-step whose A operand is 1
     // in columns 0 and 1 for every key and whose B operand holds -D split
     // into two bf16 parts (hi + lo = -D within 2^-16 relative), so the
@@ -560,33 +553,20 @@ static const void* bwd_kernel(bool dkdv, int mask, bool varlen) {
 
 template <int D>
 static hipError_t launch_bwd_d(int mask, bool varlen, const BwdParams& p, hipStream_t s) {
-    // the pre-pass runs over every query row: B*H*Nq, or H*total_q packed
-    const long rows = varlen ? (long)p.vl.H * p.vl.total_q : (long)p.BH * p.Nq;
-    if (rows > 0) {
-        constexpr int RPB = 256 / (D / 8);
-        const long grid = (rows + RPB - 1) / RPB;
-        const bf16* o = (const bf16*)p.o;
-        const bf16* dO = (const bf16*)p.dO;
-        const float* lse = p.lse;
-        float* dvec = p.dvec;
-        float* lse2 = p.lse2;
-        long r = rows;
-        void* args[] = {&o, &dO, &lse, &dvec, &lse2, &r};
-        hipError_t e = hipLaunchKernel((const void*)bwd_prep_kernel<D>, dim3((unsigned)grid), dim3(256), args, 0, s);
-        if (e != hipSuccess) return e;
-    }
     BwdParams pp = p;
     void* args[] = {&pp};
-    const long grid_kv = (long)p.BH * p.kv_slots;
-    if (grid_kv > 0) {   // with Nq == 0 the walk is empty and dK = dV = 0 are written
-        const void* fn = bwd_kernel<D>(true, mask, varlen);
-        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(256), args, 0, s);
-        if (e != hipSuccess) return e;
-    }
+    // dQ first: it also writes every query row's D and LSE * log2(e) to the
+    // workspace, which the dK/dV kernel reads (stream order)
     const long grid_q = (long)p.BH * p.q_slots;
     if (grid_q > 0) {   // with Nk == 0 every row is empty and dQ = 0 is written
         const void* fn = bwd_kernel<D>(false, mask, varlen);
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_q), dim3(256), args, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    const long grid_kv = (long)p.BH * p.kv_slots;
+    if (grid_kv > 0) {   // with Nq == 0 the walk is empty and dK = dV = 0 are written
+        const void* fn = bwd_kernel<D>(true, mask, varlen);
+        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
