@@ -52,8 +52,13 @@ __device__ __forceinline__ void pack_pairs(const float (&x)[16], u32x4& lo, u32x
 // values of LSE*log2e and D; two stages, the next one filled while the
 // current one is used.
 // ---------------------------------------------------------------------------
-template <int D, int MASK, bool VARLEN = false>
-__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParams p) {
+// PART: 0 computes dK and dV, 1 only dV (S and P^T dO), 2 only dK (S, dP,
+// dS and dS^T Q).  At d = 128 both accumulators, K and V do not fit two
+// waves per SIMD (about 440 registers), so the key side runs as a dV kernel
+// and a dK kernel, recomputing S in each, at two waves per SIMD.
+template <int D, int MASK, bool VARLEN = false, int PART = 0>
+__global__ void __launch_bounds__(256, (D == 64 || PART != 0) ? 2 : 1) bwd_dkdv_kernel(BwdParams p) {
+    constexpr bool kDV = PART != 2, kDK = PART != 1;
     constexpr int BKV = 128, BQ = 64;
     constexpr int NQB = BQ / 32;              // 32-query blocks per step
     constexpr int NQC = BQ / 16;              // 16-query k-steps
@@ -112,7 +117,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
     for (int kk = 0; kk < NKK; ++kk) {
         const uint32_t o = (uint32_t)kj * D * 2 + (16 * kk + 8 * hg) * 2;
         kreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rk, o, 0));
-        vreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rv, o, 0));
+        if constexpr (kDK) vreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rv, o, 0));
     }
 
     // Query range: the walk starts at the first query tile that sees the
@@ -171,7 +176,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         mark_loaded(kreg[kk]);
-        mark_loaded(vreg[kk]);
+        if constexpr (kDK) mark_loaded(vreg[kk]);
     }
 
     for (int qt = qt0; qt < n_qt; ++qt) {
@@ -200,13 +205,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     s[qb] = mfma_bf16(tile_read_row<D>(qs, qb * 32, kk, lane), kreg[kk], s[qb]);
-                    dp[qb] = mfma_bf16(tile_read_row<D>(dos, qb * 32, kk, lane), vreg[kk], dp[qb]);
+                    if constexpr (kDK)
+                        dp[qb] = mfma_bf16(tile_read_row<D>(dos, qb * 32, kk, lane), vreg[kk], dp[qb]);
                 }
             // At d = 128 the operand reads run four ahead of the MFMAs here and
             // two per MFMA in the products below (+4.9% on the Llama-shaped
             // backward); at d = 64 the compiler's own order measured 1.8% faster.
             if constexpr (D == 128) {
-                constexpr int nm = 2 * NKK * NQB;
+                constexpr int nm = (kDK ? 2 : 1) * NKK * NQB;
                 __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
                 for (int i = 0; i < nm - 4; ++i) {
@@ -243,31 +249,34 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
                 for (int g = 0; g < 4; ++g) {
                     const int ql = qb * 32 + g * 8 + 4 * hg;   // local query of item 4g
                     const f32x4 l2 = *(const f32x4*)(l2s + ql);
-                    const f32x4 dd = *(const f32x4*)(dds + ql);
+                    f32x4 dd = {};
+                    if constexpr (kDK) dd = *(const f32x4*)(dds + ql);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float sv = s[qb][4 * g + e];
                         const float pe = exp2_hw(fmaf(sv, p.scale_log2, -l2[e]));
                         pv[4 * g + e] = pe;
-                        dsv[4 * g + e] = pe * (dp[qb][4 * g + e] - dd[e]);
+                        if constexpr (kDK) dsv[4 * g + e] = pe * (dp[qb][4 * g + e] - dd[e]);
                     }
                 }
-                pack_pairs(pv, pw[2 * qb], pw[2 * qb + 1]);
-                pack_pairs(dsv, dsw[2 * qb], dsw[2 * qb + 1]);
+                if constexpr (kDV) pack_pairs(pv, pw[2 * qb], pw[2 * qb + 1]);
+                if constexpr (kDK) pack_pairs(dsv, dsw[2 * qb], dsw[2 * qb + 1]);
             }
             // ---- dV^T += dO^T P ;  dK^T += Q^T dS ----
 #pragma unroll
             for (int qc = 0; qc < NQC; ++qc) {
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[qc]);
-                const bf16x8 sb = __builtin_bit_cast(bf16x8, dsw[qc]);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qc * 16, db * 32, lane), pb, dvacc[db]);
-                    dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qc * 16, db * 32, lane), sb, dkacc[db]);
+                    if constexpr (kDV)
+                        dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qc * 16, db * 32, lane),
+                                              __builtin_bit_cast(bf16x8, pw[qc]), dvacc[db]);
+                    if constexpr (kDK)
+                        dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qc * 16, db * 32, lane),
+                                              __builtin_bit_cast(bf16x8, dsw[qc]), dkacc[db]);
                 }
             }
             if constexpr (D == 128) {   // two transposed reads per MFMA
-                constexpr int nm = 2 * NQC * NDB;
+                constexpr int nm = ((kDV ? 1 : 0) + (kDK ? 1 : 0)) * NQC * NDB;
                 __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
                 for (int i = 0; i < nm; ++i) {
@@ -297,13 +306,18 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(BwdParam
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int dcol = db * 32 + g * 8 + 4 * hg;
-                u32x2 wk, wv;
-                wk[0] = pack_bf16x2(dkacc[db][4 * g] * p.scale, dkacc[db][4 * g + 1] * p.scale);
-                wk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * p.scale, dkacc[db][4 * g + 3] * p.scale);
-                wv[0] = pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]);
-                wv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
-                *(u32x2*)(dKr + dcol) = wk;
-                *(u32x2*)(dVr + dcol) = wv;
+                if constexpr (kDK) {
+                    u32x2 wk;
+                    wk[0] = pack_bf16x2(dkacc[db][4 * g] * p.scale, dkacc[db][4 * g + 1] * p.scale);
+                    wk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * p.scale, dkacc[db][4 * g + 3] * p.scale);
+                    *(u32x2*)(dKr + dcol) = wk;
+                }
+                if constexpr (kDV) {
+                    u32x2 wv;
+                    wv[0] = pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]);
+                    wv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
+                    *(u32x2*)(dVr + dcol) = wv;
+                }
             }
     }
     }   // items
@@ -537,18 +551,24 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// part: -1 the dQ kernel, 0/1/2 the key-side kernel's PART
+template <int D, int MASK, bool VARLEN>
+static const void* bwd_kernel_m(int part) {
+    if (part < 0) return (const void*)bwd_dq_kernel<D, MASK, VARLEN>;
+    if constexpr (D == 64) return (const void*)bwd_dkdv_kernel<D, MASK, VARLEN, 0>;
+    else return part == 1 ? (const void*)bwd_dkdv_kernel<D, MASK, VARLEN, 1> : (const void*)bwd_dkdv_kernel<D, MASK, VARLEN, 2>;
+}
+
 template <int D, bool VARLEN>
-static const void* bwd_kernel(bool dkdv, int mask) {
-    if (mask == kMaskCausal)
-        return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskCausal, VARLEN> : (const void*)bwd_dq_kernel<D, kMaskCausal, VARLEN>;
-    if (mask == kMaskWindow)
-        return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskWindow, VARLEN> : (const void*)bwd_dq_kernel<D, kMaskWindow, VARLEN>;
-    return dkdv ? (const void*)bwd_dkdv_kernel<D, kMaskNone, VARLEN> : (const void*)bwd_dq_kernel<D, kMaskNone, VARLEN>;
+static const void* bwd_kernel(int part, int mask) {
+    if (mask == kMaskCausal) return bwd_kernel_m<D, kMaskCausal, VARLEN>(part);
+    if (mask == kMaskWindow) return bwd_kernel_m<D, kMaskWindow, VARLEN>(part);
+    return bwd_kernel_m<D, kMaskNone, VARLEN>(part);
 }
 
 template <int D>
-static const void* bwd_kernel(bool dkdv, int mask, bool varlen) {
-    return varlen ? bwd_kernel<D, true>(dkdv, mask) : bwd_kernel<D, false>(dkdv, mask);
+static const void* bwd_kernel(int part, int mask, bool varlen) {
+    return varlen ? bwd_kernel<D, true>(part, mask) : bwd_kernel<D, false>(part, mask);
 }
 
 template <int D>
@@ -559,13 +579,15 @@ static hipError_t launch_bwd_d(int mask, bool varlen, const BwdParams& p, hipStr
     // workspace, which the dK/dV kernel reads (stream order)
     const long grid_q = (long)p.BH * p.q_slots;
     if (grid_q > 0) {   // with Nk == 0 every row is empty and dQ = 0 is written
-        const void* fn = bwd_kernel<D>(false, mask, varlen);
+        const void* fn = bwd_kernel<D>(-1, mask, varlen);
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_q), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
     const long grid_kv = (long)p.BH * p.kv_slots;
-    if (grid_kv > 0) {   // with Nq == 0 the walk is empty and dK = dV = 0 are written
-        const void* fn = bwd_kernel<D>(true, mask, varlen);
+    // with Nq == 0 the walk is empty and dK = dV = 0 are written; d = 128:
+    // the dV kernel, then the dK kernel
+    for (int part = D == 64 ? 0 : 1; grid_kv > 0 && part <= (D == 64 ? 0 : 2); ++part) {
+        const void* fn = bwd_kernel<D>(part, mask, varlen);
         hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
     }
