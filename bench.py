@@ -190,7 +190,7 @@ def train_step_timing(fa, wl, steps: int, warmup: int, window=None):
             "fwd_ms": round(ms_f, 5), "fwd_tflops": round(4 * w.d * pairs / ms_f / 1e9, 3),
             "bwd_ms": round(ms_b, 5), "bwd_tflops": round(10 * w.d * pairs / ms_b / 1e9, 3),
             "bwd_flops": 10 * w.d * pairs,
-            "note": "bwd = dQ kernel (also D, LSE*log2e) + dK/dV kernel; 10*d FLOPs per "
+            "note": "bwd = dQ kernel (also D, LSE*log2e) + key-side kernel(s); 10*d FLOPs per "
                     "visible pair"}
 
 
@@ -279,7 +279,7 @@ def bench_varlen(fa, wl, w, args) -> dict:
         ms_b = time_launches(bwd, stream, 20, 5)
         result["backward"] = {"bwd_ms": round(ms_b, 5),
                               "bwd_tflops": round(10 * w.d * pairs * w.H / ms_b / 1e9, 3),
-                              "note": "fa_bwd_varlen: dQ (also D, LSE*log2e) + dK/dV; 10*d FLOPs per visible pair"}
+                              "note": "fa_bwd_varlen: dQ (also D, LSE*log2e) + key side; 10*d FLOPs per visible pair"}
     if not args.no_cpu_baseline:
         from oracle import attention_forward
         # whole (head, sequence) pairs, head by head, until ~15 s of CPU work
