@@ -139,16 +139,18 @@ def time_launches(fn, stream, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
-def train_step_timing(fa, wl, steps: int, warmup: int, window=None):
+def train_step_timing(fa, wl, steps: int, warmup: int, window=None, w=None):
     """fa_fwd then fa_bwd on the training-step workload (B=4 H=16 N=4096
-    d=64 bf16 causal), each timed on its own with HIP events; inputs, outputs
-    and the backward workspace are resident before timing starts.  With a
-    local ``window`` (wl, wr) the same shape runs fa_fwd_window and
-    fa_bwd_window instead of the causal calls."""
+    d=64 bf16 causal; or the bf16 workload ``w``, with dO drawn after its
+    inputs), each timed on its own with HIP events; inputs, outputs and the
+    backward workspace are resident before timing starts.  With a local
+    ``window`` (wl, wr) the same shape runs fa_fwd_window and fa_bwd_window
+    instead of the causal calls."""
     import torch
-    w = wl.TRAIN_STEP
+    w = wl.TRAIN_STEP if w is None else w
     dev = torch.device("cuda:0")
-    q, k, v, do = (t.to(dev) for t in wl.workload_inputs(w))
+    q, k, v, do = (t.to(dev) for t in wl.make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed,
+                                                     with_do=True))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -356,6 +358,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama_causal_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--train-workload", default="train_step_bf16",
+                    help="bf16 workload of the fwd+bwd leg (default: the training step)")
     ap.add_argument("--no-train-step", action="store_true",
                     help="skip the forward+backward timing on the training-step workload")
     ap.add_argument("--no-gemm-ceiling", action="store_true",
@@ -520,7 +524,8 @@ def main():
         gc["value_over_gemm"] = round(tflops / gc["tflops"], 4) if not decode else None
         result["mfma_ceiling"] = gc
     if not args.no_train_step:
-        result["train_step"] = train_step_timing(fa, wl, steps=20, warmup=5)
+        tw = {x.name: x for x in wl.ALL}[args.train_workload]
+        result["train_step"] = train_step_timing(fa, wl, steps=20, warmup=5, w=tw)
         if w.window is not None:
             result["train_step_window"] = train_step_timing(fa, wl, steps=20, warmup=5,
                                                             window=(1023, 0))
