@@ -99,6 +99,26 @@ def test_train_step_workload_sampled_heads():
         check_grad(to64(dv[b, h]), rv, f"dv head {bh}")
 
 
+def test_llama_causal_backward_sampled_heads():
+    """The d = 128 backward at B=4 H=32 N=4096 causal (dQ, dV and dK each from
+    their own kernel), on the inputs bench.py times with --train-workload
+    llama_causal_bf16 (the workload's seed, dO drawn after Q, K, V)."""
+    w = wl.LLAMA_CAUSAL
+    banner(w.describe() + " (backward)")
+    q, k, v, do = wl.make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, with_do=True)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, w.scale, w.causal)
+    g = torch.Generator().manual_seed(5151)
+    heads = torch.randperm(w.B * w.H, generator=g)[:2].tolist()
+    for bh in heads:
+        b, h = divmod(bh, w.H)
+        banner(f"{w.name} backward oracle head {bh}")
+        rq, rk, rv, *_ = attention_backward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]),
+                                            to64(do[b, h]), w.scale, w.causal)
+        check_grad(to64(dq[b, h]), rq, f"dq head {bh}")
+        check_grad(to64(dk[b, h]), rk, f"dk head {bh}")
+        check_grad(to64(dv[b, h]), rv, f"dv head {bh}")
+
+
 def test_backward_invariants_and_repeatability():
     banner("bwd invariants")
     q, k, v, do = wl.make_inputs(1, 2, 256, 256, 64, "bf16", seed=61, with_do=True)
