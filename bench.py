@@ -393,7 +393,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the forward shards over batch*head with no communication; see DESIGN.md)",
+              "(across GPUs the forward would shard over batch*head with no communication)",
               file=sys.stderr)
         sys.exit(2)
 
