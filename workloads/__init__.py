@@ -8,6 +8,10 @@ Recipe: a CPU ``torch.Generator`` seeded per case draws Q, K, V (then dO for
 backward) in that order with ``randn`` in float32, iid N(0, 1).  For bf16
 cases the float32 draw is cast with round-to-nearest-even (torch's cast).
 Layout is [B, H, N, d], contiguous, d innermost.  The scale is 1/sqrt(d).
+Inputs too large to draw on the host (``make_inputs_device``) follow the same
+recipe with a seeded generator on the device instead, a different stream of
+numbers from the same distribution; the oracle then reads back the heads it
+checks.
 """
 
 from __future__ import annotations
@@ -154,6 +158,24 @@ def make_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int,
         out.append(torch.randn(B, H, Nq, dv, generator=g, dtype=torch.float32))
     td = torch_dtype(dtype)
     return [t.to(td).contiguous() for t in out]
+
+
+def make_inputs_device(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int,
+                       device, with_do: bool = False, chunk_heads: int = 256):
+    """Seeded device tensors (q, k, v[, do]): a device generator draws
+    float32 N(0, 1) values a few heads at a time, cast to ``dtype`` (RNE), so
+    no full-size float32 copy is ever held."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    td = torch_dtype(dtype)
+    shapes = [(Nq, d), (Nk, d), (Nk, d)] + ([(Nq, d)] if with_do else [])
+    out = []
+    for (n, dd) in shapes:
+        t = torch.empty(B * H, n, dd, dtype=td, device=device)
+        for h0 in range(0, B * H, chunk_heads):
+            h1 = min(B * H, h0 + chunk_heads)
+            t[h0:h1] = torch.randn(h1 - h0, n, dd, generator=g, dtype=torch.float32, device=device).to(td)
+        out.append(t.view(B, H, n, dd))
+    return out
 
 
 def workload_inputs(w: Workload):
