@@ -203,9 +203,11 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
 
 
-def _check(t, name, shape, dtype):
+def _check(t, name, shape, dtype, dev):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev} (the device of q)")
     if t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -214,9 +216,20 @@ def _check(t, name, shape, dtype):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _stream():
+def _stream(dev):
+    """The current stream of q's device; calls run under a guard that makes
+    that device current, so the launch and the pointers agree."""
     import torch
-    return torch.cuda.current_stream().cuda_stream
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ws_args(workspace, dev):
+    """(pointer, size in bytes) of an optional caller-given workspace."""
+    if workspace is None:
+        return 0, 0
+    if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 def _window_args(causal, window):
@@ -242,25 +255,26 @@ def attention_forward(q, k, v, scale=None, causal=False, out=None, lse=None, wan
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     dt = q.dtype
-    _check(q, "q", (B, H, Nq, d), dt)
-    _check(k, "k", (B, H, Nk, d), dt)
-    _check(v, "v", (B, H, Nk, d), dt)
+    _check(q, "q", (B, H, Nq, d), dt, q.device)
+    _check(k, "k", (B, H, Nk, d), dt, q.device)
+    _check(v, "v", (B, H, Nk, d), dt, q.device)
     if out is None:
         out = torch.empty_like(q)
-    _check(out, "out", (B, H, Nq, d), dt)
+    _check(out, "out", (B, H, Nq, d), dt, q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     if lse is not None:
-        _check(lse, "lse", (B, H, Nq), torch.float32)
+        _check(lse, "lse", (B, H, Nq), torch.float32, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     w = _window_args(causal, window)
     lse_p = lse.data_ptr() if lse is not None else 0
-    if w is None:
-        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
-                    B, H, Nq, Nk, d, scale, causal, _dtype_code(q), _stream())
-    else:
-        st = fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
-                           B, H, Nq, Nk, d, scale, w[0], w[1], _dtype_code(q), _stream())
+    with torch.cuda.device(q.device):
+        if w is None:
+            st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
+                        B, H, Nq, Nk, d, scale, causal, _dtype_code(q), _stream(q.device))
+        else:
+            st = fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
+                               B, H, Nq, Nk, d, scale, w[0], w[1], _dtype_code(q), _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_fwd" if w is None else "fa_fwd_window")
     return out, lse
@@ -274,9 +288,9 @@ def attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0, wor
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     dt = q.dtype
-    _check(q, "q", (B, H, Nq, d), dt)
-    _check(k, "k", (B, H, Nk, d), dt)
-    _check(v, "v", (B, H, Nk, d), dt)
+    _check(q, "q", (B, H, Nq, d), dt, q.device)
+    _check(k, "k", (B, H, Nk, d), dt, q.device)
+    _check(v, "v", (B, H, Nk, d), dt, q.device)
     code = _dtype_code(q)
     out = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
@@ -284,10 +298,10 @@ def attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0, wor
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                        B, H, Nq, Nk, d, scale, causal, code, n_splits,
-                        workspace.data_ptr() if workspace is not None else 0,
-                        workspace.numel() if workspace is not None else 0, _stream())
+    with torch.cuda.device(q.device):
+        st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, Nq, Nk, d, scale, causal, code, n_splits,
+                            *_ws_args(workspace, q.device), _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_fwd_splitkv")
     return out, lse
@@ -304,8 +318,8 @@ def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=
     dt = q.dtype
     for t, n, s in ((q, "q", (B, H, Nq, d)), (k, "k", (B, H, Nk, d)), (v, "v", (B, H, Nk, d)),
                     (o, "o", (B, H, Nq, d)), (do, "do", (B, H, Nq, d))):
-        _check(t, n, s, dt)
-    _check(lse, "lse", (B, H, Nq), torch.float32)
+        _check(t, n, s, dt, q.device)
+    _check(lse, "lse", (B, H, Nq), torch.float32, q.device)
     code = _dtype_code(q)
     need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, code)
     if workspace is None and need > 0:
@@ -315,12 +329,12 @@ def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=
     w = _window_args(causal, window)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
-    ws = (workspace.data_ptr() if workspace is not None else 0,
-          workspace.numel() if workspace is not None else 0)
-    if w is None:
-        st = fa_bwd(*ptrs, B, H, Nq, Nk, d, scale, causal, code, *ws, _stream())
-    else:
-        st = fa_bwd_window(*ptrs, B, H, Nq, Nk, d, scale, w[0], w[1], code, *ws, _stream())
+    ws = _ws_args(workspace, q.device)
+    with torch.cuda.device(q.device):
+        if w is None:
+            st = fa_bwd(*ptrs, B, H, Nq, Nk, d, scale, causal, code, *ws, _stream(q.device))
+        else:
+            st = fa_bwd_window(*ptrs, B, H, Nq, Nk, d, scale, w[0], w[1], code, *ws, _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_bwd" if w is None else "fa_bwd_window")
     return dq, dk, dv
@@ -357,23 +371,24 @@ def attention_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
     H, Tq, d = q.shape
     Tk = k.shape[1]
     B = cu_seqlens_q.numel() - 1
-    _check(q, "q", (H, Tq, d), q.dtype)
-    _check(k, "k", (H, Tk, d), q.dtype)
-    _check(v, "v", (H, Tk, d), q.dtype)
+    _check(q, "q", (H, Tq, d), q.dtype, q.device)
+    _check(k, "k", (H, Tk, d), q.dtype, q.device)
+    _check(v, "v", (H, Tk, d), q.dtype, q.device)
     _check_cu(cu_seqlens_q, "cu_seqlens_q", B, q.device)
     _check_cu(cu_seqlens_k, "cu_seqlens_k", B, q.device)
     if out is None:
         out = torch.empty_like(q)
-    _check(out, "out", (H, Tq, d), q.dtype)
+    _check(out, "out", (H, Tq, d), q.dtype, q.device)
     if lse is None:
         lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
-    _check(lse, "lse", (H, Tq), torch.float32)
+    _check(lse, "lse", (H, Tq), torch.float32, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     wl, wr = _mask_args(causal, window)
-    st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Tq, Tk,
-                       int(max_seqlen_q), int(max_seqlen_k), d, scale, wl, wr, _dtype_code(q),
-                       _stream())
+    with torch.cuda.device(q.device):
+        st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Tq, Tk,
+                           int(max_seqlen_q), int(max_seqlen_k), d, scale, wl, wr, _dtype_code(q),
+                           _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_fwd_varlen")
     return out, lse
@@ -390,8 +405,8 @@ def attention_backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, m
     B = cu_seqlens_q.numel() - 1
     for t, n, s in ((q, "q", (H, Tq, d)), (k, "k", (H, Tk, d)), (v, "v", (H, Tk, d)),
                     (o, "o", (H, Tq, d)), (do, "do", (H, Tq, d))):
-        _check(t, n, s, q.dtype)
-    _check(lse, "lse", (H, Tq), torch.float32)
+        _check(t, n, s, q.dtype, q.device)
+    _check(lse, "lse", (H, Tq), torch.float32, q.device)
     _check_cu(cu_seqlens_q, "cu_seqlens_q", B, q.device)
     _check_cu(cu_seqlens_k, "cu_seqlens_k", B, q.device)
     code = _dtype_code(q)
@@ -401,12 +416,12 @@ def attention_backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, m
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     wl, wr = _mask_args(causal, window)
-    st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                       do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Tq, Tk,
-                       int(max_seqlen_q), int(max_seqlen_k), d, scale, wl, wr, code,
-                       workspace.data_ptr() if workspace is not None else 0,
-                       workspace.numel() if workspace is not None else 0, _stream())
+    with torch.cuda.device(q.device):
+        st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Tq, Tk,
+                           int(max_seqlen_q), int(max_seqlen_k), d, scale, wl, wr, code,
+                           *_ws_args(workspace, q.device), _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_bwd_varlen")
     return dq, dk, dv

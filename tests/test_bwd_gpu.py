@@ -133,3 +133,22 @@ def test_backward_invariants_and_repeatability():
     vs = dv1.float().sum(dim=2).cpu()
     ds = do.float().sum(dim=2)
     assert torch.max(torch.abs(vs - ds)).item() <= 2e-2 * max(1.0, ds.abs().max().item())
+
+
+def test_binding_checks_devices_and_sizes_workspace_in_bytes():
+    banner("binding: device checks, workspace in bytes")
+    q, k, v, do = wl.make_inputs(1, 2, 100, 100, 64, "bf16", seed=71, with_do=True)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    with pytest.raises(ValueError):
+        fa.attention_forward(qd, k, vd, causal=True)          # k left on the host
+    o, lse = fa.attention_forward(qd, kd, vd, causal=True)
+    need = fa.fa_bwd_workspace_bytes(1, 2, 100, 100, 64, fa.FA_BF16)
+    with pytest.raises(ValueError):
+        fa.attention_backward(qd, kd, vd, o, lse, dod, causal=True,
+                              workspace=torch.empty(need, dtype=torch.uint8))
+    # a float32 workspace: at least `need` bytes in fewer than `need` elements
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
+    dq, dk, dv = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=True, workspace=ws)
+    dq0, dk0, dv0 = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq0) and torch.equal(dk, dk0) and torch.equal(dv, dv0)
