@@ -157,36 +157,37 @@ __device__ __forceinline__ void async_load_lds16(i32x4 rsrc, uint32_t lds_addr, 
 // Eight such copies in one statement: 1 KiB each to LDS addresses
 // lds_addr, lds_addr + STEP, ... (STEP >= 1024: consecutive pieces, or
 // pieces with padding between them) from per-lane offsets off[i] + soff.
-// M0 is bound as an input (the compiler writes it); the statement steps it
-// by STEP per copy and steps it back at the end, so M0 leaves the statement
-// holding the value the compiler put there.  The wait states are paid once
-// up front (5: VALU write of an SGPR operand before the statement), then 1
-// after each M0 step.
+// M0 is a tied input/output operand: the compiler writes lds_addr into it
+// before the statement, the statement steps it by STEP per copy, and the
+// compiler regards it as changed afterwards.  The compiler's hazard checks
+// do not look inside the statement, so it pays the wait states itself:
+// 5 up front (a VALU write of an SGPR operand -- v_readfirstlane -- before
+// a buffer load that reads it) and 1 after each M0 step (an SALU write of M0
+// before an LDS-direct load), as gfx950 requires.
 template <uint32_t STEP = 1024>
 __device__ __forceinline__ void async_load_lds16_x8(i32x4 rsrc, uint32_t lds_addr, const uint32_t (&off)[8],
                                                     uint32_t soff) {
+    uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile(
         "s_nop 4\n\t"
-        "buffer_load_dwordx4 %0, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %3, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %4, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %5, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %6, %8, %9 offen lds\n\t"
-        "s_add_u32 m0, m0, %11\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %7, %8, %9 offen lds\n\t"
-        "s_sub_u32 m0, m0, %12"
-        :
-        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "v"(off[5]), "v"(off[6]),
-          "v"(off[7]), "s"(rsrc), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)),
-          "i"(STEP), "i"(7 * STEP)
+        "buffer_load_dwordx4 %[o0], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o1], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o2], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o3], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o4], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o5], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o6], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o7], %[rs], %[so] offen lds"
+        : [m0] "+{m0}"(m0)
+        : [o0] "v"(off[0]), [o1] "v"(off[1]), [o2] "v"(off[2]), [o3] "v"(off[3]), [o4] "v"(off[4]),
+          [o5] "v"(off[5]), [o6] "v"(off[6]), [o7] "v"(off[7]), [rs] "s"(rsrc), [so] "s"(soff), [st] "i"(STEP)
         : "memory", "scc");
 }
 
@@ -194,19 +195,19 @@ __device__ __forceinline__ void async_load_lds16_x8(i32x4 rsrc, uint32_t lds_add
 template <uint32_t STEP = 1024>
 __device__ __forceinline__ void async_load_lds16_x4(i32x4 rsrc, uint32_t lds_addr, const uint32_t (&off)[4],
                                                     uint32_t soff) {
+    uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile(
         "s_nop 4\n\t"
-        "buffer_load_dwordx4 %0, %4, %5 offen lds\n\t"
-        "s_add_u32 m0, m0, %7\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %4, %5 offen lds\n\t"
-        "s_add_u32 m0, m0, %7\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %4, %5 offen lds\n\t"
-        "s_add_u32 m0, m0, %7\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %3, %4, %5 offen lds\n\t"
-        "s_sub_u32 m0, m0, %8"
-        :
-        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(rsrc), "s"(soff),
-          "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)), "i"(STEP), "i"(3 * STEP)
+        "buffer_load_dwordx4 %[o0], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o1], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o2], %[rs], %[so] offen lds\n\t"
+        "s_add_u32 m0, m0, %[st]\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %[o3], %[rs], %[so] offen lds"
+        : [m0] "+{m0}"(m0)
+        : [o0] "v"(off[0]), [o1] "v"(off[1]), [o2] "v"(off[2]), [o3] "v"(off[3]), [rs] "s"(rsrc), [so] "s"(soff),
+          [st] "i"(STEP)
         : "memory", "scc");
 }
 

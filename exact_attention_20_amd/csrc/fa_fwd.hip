@@ -57,10 +57,12 @@ constexpr float kRescaleSlack = 8.0f;
 // keep that base and skip the row maximum.  Any base gives the same O / l
 // and m + log l in exact arithmetic; in floating point P, l and O~ keep their
 // relative precision whatever the base, so the only hazard of a base below
-// the true maximum is overflow.  A row whose lane-local running sum ends the
-// query tile outside [0, kFastSumLimit] (overflow, or NaN inputs) marks the
-// wave, and the workgroup then recomputes the query tile with the per-tile
-// maximum and the conditional rescale above.
+// the true maximum is overflow, of l or of O~ = sum P V (which can overflow
+// with l in range when |V| is beyond about 2^64).  A row whose lane-local
+// running sum ends the query tile outside [0, kFastSumLimit], or whose O~
+// accumulators are not all finite (overflow, or NaN inputs), marks the wave,
+// and the workgroup then recomputes the query tile with the per-tile maximum
+// and the conditional rescale above.
 constexpr float kFastSumLimit = 0x1p64f;
 
 // SPLIT: split-KV mode.  The key tiles of each query tile are divided into
@@ -368,8 +370,15 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         // both LDS buffers are reloaded (the recomputation's last tile
         // fetches the next item's first tile again).
         // l_run only grows (a sum of terms >= 0; inf and NaN persist), so its
-        // final value is checked once, after the last tile
-        const bool bad = __builtin_amdgcn_ballot_w64(!(l_run <= kFastSumLimit)) != 0;
+        // final value is checked once, after the last tile; the O~
+        // accumulators by their sum (inf and NaN propagate through it; a
+        // finite sum that overflows only costs a recomputation)
+        float osum = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) osum += oacc[db][i];
+        const bool bad = __builtin_amdgcn_ballot_w64(!(l_run <= kFastSumLimit) || !(fabsf(osum) <= 0x1.fffffep127f)) != 0;
         if (lane == 0) redo_flag[wave] = bad ? 1 : 0;
         tile_barrier();
         if ((redo_flag[0] | redo_flag[1] | redo_flag[2] | redo_flag[3]) != 0) {

@@ -168,3 +168,41 @@ def test_planted_jump_in_varlen_batch():
     o_ref, lse_ref = varlen_forward(to64(q), to64(k), to64(v), np.array(cu), np.array(cu), scale,
                                     causal=True)
     check_forward(to64(o), to64(lse), o_ref, lse_ref, "bf16", "varlen planted")
+
+
+BIG_V_CASES = [
+    # B, H, N, d, causal
+    (1, 3, 700, 128, True),
+    (1, 3, 700, 128, False),
+    (2, 2, 520, 64, True),
+    (2, 2, 520, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", BIG_V_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_planted_jump_with_huge_values(case):
+    """A logit jump of ~55 log2 units keeps the row sum below 2^64 (the sum
+    check passes), but with V = 1e30 at the planted key O~ = sum P V
+    overflows fp32 on the fixed base; the accumulator check must send the
+    query tile to the recomputation.  Compared relative to |O_ref|, since
+    the outputs are ~1e30."""
+    B, H, N, d, causal = case
+    banner(f"fwd planted jump, huge V {case}")
+    q, k, v = wl.make_inputs(B, H, N, N, d, "bf16", seed=4800 + N + d)
+    rows = planted_rows(B, H, N, 4, seed=4801 + N)
+    A = plant(q, k, rows, 55, d)
+    for (b, h, r) in rows:
+        v[b, h, r, 0] = 1e30
+        v[b, h, r, d - 1] = -1e30
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_forward(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all(), f"{case}: non-finite output"
+    for (b, h) in sorted({(b, h) for (b, h, _) in rows}):
+        o_ref, lse_ref = attention_forward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), scale, causal)
+        ref = max(1.0, float(np.max(np.abs(o_ref))))
+        err = float(np.max(np.abs(to64(o[b, h]) - o_ref)))
+        assert err <= 2e-2 * ref, f"{case} head {(b, h)} A={A}: O err {err:.3e} vs |O_ref| {ref:.3e}"
+        err_l = float(np.max(np.abs(to64(lse[b, h]) - lse_ref)))
+        assert err_l <= 1e-3, f"{case} head {(b, h)}: LSE err {err_l:.3e}"
