@@ -20,7 +20,12 @@ timing one launch at a time after flushing L2 and the Infinity Cache.
 ``mfma_ceiling`` times an 8192^3 bf16 torch.matmul (hipBLASLt) on the same GPU:
 the MFMA rate the vendor library sustains, as context for ``roofline.frac``.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
-workload on the host cores.
+workload on the host cores (core count and CPU model stated); that leg runs
+before the timing and also compares the sampled heads of the GPU's own output
+with the oracle (``parity``; a failure exits non-zero).  ``samples`` gives the
+per-launch median, min and interquartile range of the K timed launches;
+``device`` the GPU and software stack; ``mfma_ceiling.probe`` the bf16 MFMA rate
+and core clock this GPU sustains under a pure MFMA load (libfa_probe.so).
 """
 
 from __future__ import annotations
@@ -102,26 +107,147 @@ def blas_threads() -> int:
         return 1
 
 
-def cpu_baseline(w, q, k, v, target_s: float = 15.0):
+def host_description() -> dict:
+    """The host cores the oracle runs on: logical CPUs, the ones this process
+    may use, and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count()
+    return {"nproc": os.cpu_count(), "affinity_cores": affinity, "cpu_model": model}
+
+
+def cpu_baseline(w, q, k, v, target_s: float = 15.0, o_gpu=None, lse_gpu=None):
     """Time the fp64 oracle (as it stands) on whole heads of the workload until
-    about ``target_s`` seconds of CPU work; report its causal-adjusted rate."""
+    about ``target_s`` seconds of CPU work; report its causal-adjusted rate.
+    With the GPU's outputs of the same workload (host tensors), every head the
+    oracle computes is also compared with them at the parity tolerances (the
+    check that precedes the GPU timing)."""
     import numpy as np
     from oracle import attention_forward
     threads = blas_threads()
     per_head_flops = fwd_flops(w) / (w.B * w.H)
     done, t_total = 0, 0.0
     heads = w.B * w.H
+    err_o, err_l, ref_o, ref_l = 0.0, 0.0, 0.0, 1.0
     while done < heads and t_total < target_s:
         b, h = divmod(done, w.H)
         qh, kh, vh = (t[b, h].double().numpy() for t in (q, k, v))
         t0 = time.perf_counter()
-        attention_forward(qh, kh, vh, w.scale, w.causal, window=w.window)
+        o_ref, lse_ref = attention_forward(qh, kh, vh, w.scale, w.causal, window=w.window)
         t_total += time.perf_counter() - t0
+        if o_gpu is not None:
+            live = ~np.isneginf(lse_ref)
+            err_o = max(err_o, float(np.max(np.abs(o_gpu[b, h].double().numpy() - o_ref))))
+            ref_o = max(ref_o, float(np.max(np.abs(o_ref))))
+            if live.any():
+                err_l = max(err_l, float(np.max(np.abs(lse_gpu[b, h].double().numpy()[live] - lse_ref[live]))))
+                ref_l = max(ref_l, float(np.max(np.abs(lse_ref[live]))))
         done += 1
     rate = per_head_flops * done / t_total / 1e12
-    return {"value": round(rate, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {heads} (batch, head) pairs of {w.describe()}, fp64 NumPy, "
-                      f"{t_total:.1f} s; numpy exp single-threaded, BLAS {threads} threads"}
+    res = {"value": round(rate, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} of {heads} (batch, head) pairs of {w.describe()}, fp64 NumPy, "
+                     f"{t_total:.1f} s; numpy exp single-threaded, BLAS {threads} threads",
+           "blas_threads": threads, **host_description()}
+    parity = None
+    if o_gpu is not None:
+        if w.dtype == "bf16":
+            tol = {"o_abs": 2e-2, "lse_abs": 1e-3}
+            ok = err_o <= tol["o_abs"] and err_l <= tol["lse_abs"]
+        else:   # fp32: relative to the largest reference magnitude
+            tol = {"o_rel": 1e-5, "lse_rel": 1e-5}
+            ok = err_o <= tol["o_rel"] * ref_o and err_l <= tol["lse_rel"] * ref_l
+        parity = {"heads_checked": done, "heads": heads, "o_max_abs_err": err_o, "lse_max_abs_err": err_l,
+                  "tolerance": tol, "ok": bool(ok),
+                  "note": "whole heads of the timed workload's own output against the fp64 oracle, "
+                          "before the timed launches"}
+    return res, parity
+
+
+def timed_launches(fn, stream, steps: int):
+    """K back-to-back launches of ``fn`` with a HIP event recorded on
+    ``stream`` before each and after the last, bracketed by device
+    synchronisation.  Returns the mean ms per launch over the whole region
+    (the step time) and the per-launch samples' median, min and
+    interquartile range."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i].record(stream)
+        fn()
+    ev[steps].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    total = ev[0].elapsed_time(ev[steps])
+
+    def q(f):
+        x = f * (len(per) - 1)
+        lo = int(math.floor(x))
+        hi = min(lo + 1, len(per) - 1)
+        return per[lo] + (per[hi] - per[lo]) * (x - lo)
+
+    return total / steps, {"n": steps, "median_ms": round(q(0.5), 5), "min_ms": round(per[0], 5),
+                           "iqr_ms": round(q(0.75) - q(0.25), 5), "p25_ms": round(q(0.25), 5),
+                           "p75_ms": round(q(0.75), 5)}
+
+
+def device_description() -> dict:
+    """The GPU, its architecture and compute units, and the software stack."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": rocm, "hip": torch.version.hip,
+            "torch": torch.__version__}
+
+
+def mfma_probe(grid: int = 1024, iters: int = 4000, repeats: int = 3) -> dict:
+    """The bf16 MFMA rate this GPU sustains under a pure MFMA load
+    (libfa_probe.so: four waves per SIMD, 16 independent 32x32x16 MFMAs per
+    round, no memory traffic) and the core clock meanwhile (s_memtime against
+    the 100 MHz s_memrealtime), median of ``repeats`` launches."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_20_amd", "libfa_probe.so"))
+    lib.fa_probe_mfma_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+    lib.fa_probe_mfma_flops.restype = ctypes.c_double
+    lib.fa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda:0")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    flops = lib.fa_probe_mfma_flops(grid, iters)
+    res = []
+    for _ in range(repeats + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.fa_probe_mfma_launch(ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(clocks.data_ptr()),
+                                      grid, iters, ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if st != 0:
+            raise RuntimeError(f"fa_probe_mfma_launch failed with {st}")
+        cyc, ticks = (int(x) for x in clocks.cpu().tolist())
+        res.append((flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, cyc / (ticks / 100e6) / 1e9))
+    res = sorted(res[1:])
+    tf, ghz = res[len(res) // 2]
+    return {"op": "libfa_probe: 32x32x16 bf16 MFMA chains, 4 waves/SIMD, no memory traffic",
+            "tflops": round(tf, 1), "sclk_ghz": round(ghz, 3), "frac_of_published": round(tf / PEAK["bf16"], 4)}
 
 
 def time_launches(fn, stream, steps: int, warmup: int) -> float:
@@ -299,7 +425,8 @@ def bench_varlen(fa, wl, w, args) -> dict:
             "value": round(4 * w.d * done_pairs / t_total / 1e12, 6), "unit": "TFLOP/s",
             "cores": blas_threads(), "kind": "oracle",
             "sample": f"{done} of {w.H * len(L)} (head, sequence) pairs, fp64 NumPy, "
-                      f"{t_total:.1f} s; numpy exp single-threaded"}
+                      f"{t_total:.1f} s; numpy exp single-threaded",
+            "blas_threads": blas_threads(), **host_description()}
     return result
 
 
@@ -448,17 +575,21 @@ def main():
             if st != 0:
                 raise fa.FAError(st, "fa_fwd_splitkv")
 
+    # Parity first (the cpu_baseline leg): one launch, its output against the
+    # fp64 oracle on every head the bounded CPU sample reaches.
+    cpu_res, parity = None, None
+    if not args.no_cpu_baseline:
+        step()
+        torch.cuda.synchronize()
+        cpu_res, parity = cpu_baseline(w, q, k, v, o_gpu=o.cpu(), lse_gpu=lse.cpu())
+        if parity is not None and not parity["ok"]:
+            print(json.dumps({"error": "parity check failed before timing", "parity": parity}), flush=True)
+            sys.exit(1)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms = ms_total / args.steps
+    ms, samples = timed_launches(step, stream, args.steps)
     flops = fwd_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK[w.dtype]
@@ -488,8 +619,13 @@ def main():
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
+        "samples": {**samples, "median_tflops": round(flops / (samples["median_ms"] * 1e-3) / 1e12, 3),
+                    "note": "per-launch HIP events inside the timed region; value and ms_per_step are "
+                            "the mean over the whole region"},
         "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "peak_GBps": 8000.0, "note": "algorithmic bytes / launch time, warm caches"},
+        "device": device_description(),
+        "parity": parity if parity is not None else {"ok": None, "note": "skipped with --no-cpu-baseline"},
     }
     if decode:
         gbps = nbytes / (ms * 1e-3) / 1e9
@@ -522,6 +658,9 @@ def main():
     if w.dtype == "bf16" and not args.no_gemm_ceiling:
         gc = gemm_ceiling()
         gc["value_over_gemm"] = round(tflops / gc["tflops"], 4) if not decode else None
+        pr = mfma_probe()
+        pr["value_over_probe"] = round(tflops / pr["tflops"], 4) if not decode else None
+        gc["probe"] = pr
         result["mfma_ceiling"] = gc
     if not args.no_train_step:
         tw = {x.name: x for x in wl.ALL}[args.train_workload]
@@ -529,8 +668,8 @@ def main():
         if w.window is not None:
             result["train_step_window"] = train_step_timing(fa, wl, steps=20, warmup=5,
                                                             window=(1023, 0))
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    if cpu_res is not None:
+        result["cpu_baseline"] = cpu_res
     print(json.dumps(result), flush=True)
 
 

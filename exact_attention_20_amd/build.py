@@ -1,4 +1,5 @@
-"""Build libfa.so (the C-ABI library) in-tree with hipcc for gfx950.
+"""Build libfa.so (the C-ABI library) in-tree with hipcc for gfx950, and the
+MFMA throughput probe libfa_probe.so that bench.py reports beside the roofline.
 
     python -m exact_attention_20_amd.build
 
@@ -60,6 +61,13 @@ def build(verbose: bool = False, extra=()) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    # the MFMA throughput probe bench.py reports beside the roofline
+    probe = os.path.join(PKG, "libfa_probe.so")
+    cmd = [cc, *flags(extra), "-x", "hip", "-shared", os.path.join(CSRC, "probe_mfma.hip"), "-o", probe + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(probe + ".tmp", probe)
     return LIB
 
 

@@ -1,0 +1,59 @@
+// MFMA throughput probe (libfa_probe.so): the rate the bf16 matrix cores
+// sustain on this GPU under a pure MFMA load, and the core clock while they
+// do.  bench.py reports it beside the published 2.5 PFLOP/s peak as a
+// measured denominator.  Not part of the attention library.
+//
+// Each wave runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 on four
+// independent accumulator chains (no memory traffic inside the loop), so the
+// issue rate is the matrix cores' own.  Wave 0 of workgroup 0 records
+// s_memtime (core clock) and s_memrealtime (a fixed 100 MHz reference)
+// before and after its loop.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(256) probe_mfma_kernel(float* out, uint64_t* clocks, int iters) {
+    const int lane = threadIdx.x & 63;
+    bf16x8_t a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * lane + 0.01f * i);
+        b[i] = (__bf16)(0.01f * i);
+    }
+    f32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+        }
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    float s = 0.f;
+    for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;   // keeps the products live
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        clocks[0] = t1 - t0;
+        clocks[1] = r1 - r0;
+    }
+}
+
+// out: grid * 256 floats; clocks: 2 uint64 (core cycles, 100 MHz ticks of
+// wave 0 of workgroup 0).  Returns 0, or -7 if the launch failed.
+extern "C" int fa_probe_mfma_launch(void* out, void* clocks, int grid, int iters, void* stream) {
+    if (!out || !clocks || grid <= 0 || iters <= 0) return -1;
+    hipLaunchKernelGGL(probe_mfma_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (float*)out,
+                       (uint64_t*)clocks, iters);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+// FLOPs one launch executes: grid * 4 waves * iters * 16 MFMAs * 32768.
+extern "C" double fa_probe_mfma_flops(int grid, int iters) {
+    return (double)grid * 4.0 * (double)iters * 16.0 * 32768.0;
+}

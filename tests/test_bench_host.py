@@ -75,3 +75,35 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_host_description_states_cores_and_model():
+    h = bench.host_description()
+    assert h["nproc"] == os.cpu_count() and h["nproc"] >= 1
+    assert 1 <= h["affinity_cores"] <= h["nproc"]
+    assert isinstance(h["cpu_model"], str) and h["cpu_model"]
+
+
+def test_cpu_baseline_parity_leg_flags_a_wrong_output():
+    """The parity check that precedes the timing: the oracle's own output
+    passes, the same output with one element moved by 0.05 (beyond the bf16
+    bar of 2e-2 on O) fails, and so does an LSE moved by 2e-3 (bar 1e-3)."""
+    import torch
+    from oracle import attention_forward
+    w = wl.Workload("tiny", 1, 2, 40, 40, 64, "bf16", True, seed=77)
+    q, k, v = wl.make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)
+    o = torch.zeros(w.B, w.H, w.Nq, w.d, dtype=torch.float64)
+    lse = torch.zeros(w.B, w.H, w.Nq, dtype=torch.float64)
+    for h in range(w.H):
+        oh, lh = attention_forward(q[0, h].double().numpy(), k[0, h].double().numpy(),
+                                   v[0, h].double().numpy(), w.scale, w.causal)
+        o[0, h], lse[0, h] = torch.from_numpy(oh), torch.from_numpy(lh)
+    res, par = bench.cpu_baseline(w, q, k, v, target_s=30.0, o_gpu=o, lse_gpu=lse)
+    assert par["ok"] and par["heads_checked"] == 2 and par["o_max_abs_err"] == 0.0
+    assert res["cores"] >= 1 and res["nproc"] == os.cpu_count() and "cpu_model" in res
+    bad = o.clone()
+    bad[0, 1, 17, 5] += 0.05
+    assert not bench.cpu_baseline(w, q, k, v, target_s=30.0, o_gpu=bad, lse_gpu=lse)[1]["ok"]
+    badl = lse.clone()
+    badl[0, 0, 3] += 2e-3
+    assert not bench.cpu_baseline(w, q, k, v, target_s=30.0, o_gpu=o, lse_gpu=badl)[1]["ok"]
