@@ -82,13 +82,19 @@ def test_backward_paired_tiles_sampled_heads(case):
         check_grad(to64(dv[b, h]), rv, f"dv {case} head {bh}")
 
 
+def sampled_heads(w, seed, n=16):
+    """The first and the last (batch, head) and n-2 others drawn with ``seed``."""
+    g = torch.Generator().manual_seed(seed)
+    others = [bh for bh in torch.randperm(w.B * w.H, generator=g).tolist() if bh not in (0, w.B * w.H - 1)]
+    return [0, w.B * w.H - 1] + others[: n - 2]
+
+
 def test_train_step_workload_sampled_heads():
     w = wl.TRAIN_STEP
     banner(w.describe())
     q, k, v, do = wl.workload_inputs(w)
     dq, dk, dv = gpu_fwd_bwd(q, k, v, do, w.scale, w.causal)
-    g = torch.Generator().manual_seed(5050)
-    heads = torch.randperm(w.B * w.H, generator=g)[:3].tolist()
+    heads = sampled_heads(w, 5050)
     for bh in heads:
         b, h = divmod(bh, w.H)
         banner(f"{w.name} oracle head {bh}")
@@ -107,8 +113,7 @@ def test_llama_causal_backward_sampled_heads():
     banner(w.describe() + " (backward)")
     q, k, v, do = wl.make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, with_do=True)
     dq, dk, dv = gpu_fwd_bwd(q, k, v, do, w.scale, w.causal)
-    g = torch.Generator().manual_seed(5151)
-    heads = torch.randperm(w.B * w.H, generator=g)[:2].tolist()
+    heads = sampled_heads(w, 5151)
     for bh in heads:
         b, h = divmod(bh, w.H)
         banner(f"{w.name} backward oracle head {bh}")
