@@ -13,6 +13,8 @@ Raw entry points, same names and argument order as ``include/fa.h``:
     fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal,
            dtype, workspace, workspace_bytes, stream) -> int
     fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) -> int
+    fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype,
+                   stream) -> int
     fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, d, scale, window_left, window_right,
                   dtype, stream) -> int
     fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, window_left,
@@ -54,7 +56,7 @@ import os
 __all__ = [
     "FA_F32", "FA_BF16", "FAError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_bwd_window", "fa_fwd_varlen",
+    "fa_bwd_workspace_bytes", "fa_bwd_noalloc", "fa_fwd_window", "fa_bwd_window", "fa_fwd_varlen",
     "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_strerror",
     "attention_forward_varlen", "attention_backward_varlen",
     "attention_forward", "attention_forward_splitkv", "attention_backward",
@@ -97,6 +99,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
@@ -142,6 +146,13 @@ def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtyp
     return load_library().fa_bwd(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq), _p(dk),
                                  _p(dv), B, H, Nq, Nk, d, float(scale), int(causal), int(dtype),
                                  _p(workspace), int(workspace_bytes), _p(stream))
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype,
+                   stream) -> int:
+    return load_library().fa_bwd_noalloc(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
+                                         _p(dk), _p(dv), B, H, Nq, Nk, d, float(scale), int(causal),
+                                         int(dtype), _p(stream))
 
 
 def fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) -> int:

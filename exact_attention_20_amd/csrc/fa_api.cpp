@@ -172,6 +172,23 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
     return hip_status(fa::launch_fwd_split(d, causal != 0, p, (hipStream_t)stream));
 }
 
+int fa::bwd_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dO, const void* dq, const void* dk, const void* dv, int B, int H,
+                       int Nq, int Nk, int d, float scale, int dtype, bool* work) {
+    *work = false;
+    const int st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if ((long)B * H == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
+    const bool has_q = Nq > 0, has_k = Nk > 0;
+    if ((has_q && (!q || !o || !lse || !dO || !dq)) || (has_k && (!k || !v || !dk || !dv))) return FA_ERR_NULL;
+    if (has_q && (!aligned16(q) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) || !aligned4(lse)))
+        return FA_ERR_ALIGN;
+    if (has_k && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))) return FA_ERR_ALIGN;
+    *work = true;
+    return FA_OK;
+}
+
 extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
     if (check_common(B, H, Nq, Nk, d, 1.0f, dtype) != FA_OK) return 0;
     if (dtype != FA_BF16) return 0;
@@ -186,16 +203,10 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dO, void* dq, void* dk, void* dv,
              int B, int H, int Nq, int Nk, int d, float scale, Mask mask,
              int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-    int st = check_common(B, H, Nq, Nk, d, scale, dtype);
-    if (st != FA_OK) return st;
-    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    bool work = false;
+    int st = fa::bwd_check_args(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, dtype, &work);
+    if (st != FA_OK || !work) return st;
     const long BH = (long)B * H;
-    if (BH == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
-    const bool has_q = Nq > 0, has_k = Nk > 0;
-    if ((has_q && (!q || !o || !lse || !dO || !dq)) || (has_k && (!k || !v || !dk || !dv))) return FA_ERR_NULL;
-    if (has_q && (!aligned16(q) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) || !aligned4(lse)))
-        return FA_ERR_ALIGN;
-    if (has_k && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))) return FA_ERR_ALIGN;
     const size_t need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
@@ -412,6 +423,7 @@ extern "C" const char* fa_strerror(int status) {
         case FA_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
         case FA_ERR_SCALE: return "scale must be finite and > 0";
         case FA_ERR_WINDOW: return "window reaches must be >= 0, or -1 for an unbounded side";
+        case FA_ERR_SCRATCH: return "the call needs more than fa_bwd_noalloc's static buffer (FA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

@@ -94,6 +94,12 @@ bool fwd_pair_tiles(int dtype, int d, bool causal, long bh, int n_qtiles);
 // The same decision for the backward kernels' key and query tiles.
 bool bwd_pair_tiles(bool causal, long bh, int n_tiles);
 
+// fa_bwd's checks of everything but the workspace (status codes of fa.h);
+// *work is false when the call has nothing to compute.  No HIP call.
+int bwd_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, const void* dq, const void* dk, const void* dv, int B, int H,
+                   int Nq, int Nk, int d, float scale, int dtype, bool* work);
+
 hipError_t launch_fwd(int dtype, int d, int mask, FwdParams p, hipStream_t stream);
 // bf16 forward over a variable-length batch (p.vl); grid B*H*n_slots.
 hipError_t launch_fwd_varlen(int d, int mask, FwdParams p, hipStream_t stream);

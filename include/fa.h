@@ -34,7 +34,8 @@
  *          no visible key gets O = 0 and LSE = -inf and contributes nothing
  *          to the gradients.
  * Memory   the caller owns all device memory.  The library allocates nothing,
- *          frees nothing and keeps no pointer after returning.  Pointers to
+ *          frees nothing and keeps no pointer after returning (the one
+ *          exception: fa_bwd_noalloc's static per-device array).  Pointers to
  *          tensors must be 16-byte aligned device pointers; lse 4-byte aligned.
  * Streams  `stream` is a hipStream_t (NULL = the null stream).  Work is
  *          enqueued asynchronously; no host synchronisation happens.  Faults
@@ -70,7 +71,8 @@ typedef enum {
     FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required       */
     FA_ERR_LAUNCH = -7,     /* the HIP runtime refused a kernel launch       */
     FA_ERR_SCALE = -8,      /* scale is not finite or not > 0                */
-    FA_ERR_WINDOW = -9      /* a window reach below -1                       */
+    FA_ERR_WINDOW = -9,     /* a window reach below -1                       */
+    FA_ERR_SCRATCH = -10    /* beyond fa_bwd_noalloc's static buffer         */
 } fa_status_t;
 
 /* Largest Nq or Nk accepted (keeps every in-head byte offset within 32 bits). */
@@ -151,6 +153,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dO, void* dq, void* dk, void* dv,
            int B, int H, int Nq, int Nk, int d, float scale, int causal,
            int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * arguments and results as fa_bwd (bitwise the same outputs), without the
+ * workspace: its two row vectors live in a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES held by each GPU the library runs on until the
+ * process ends.  The call allocates and frees nothing.
+ *
+ * Limit: fa_bwd_workspace_bytes() of the call must not exceed
+ * FA_NOALLOC_SCRATCH_BYTES, i.e. B * H * Nq <= 1,048,576 query rows (e.g.
+ * B=8 H=32 N=4096, or B=1 H=32 N=32768); beyond it the call returns
+ * FA_ERR_SCRATCH and enqueues nothing.  The first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress, with the device
+ * current).  Every call on one GPU shares its array, so calls that overlap on
+ * one GPU (other streams, other host threads) race and must be ordered by the
+ * caller; nothing in the array needs clearing between calls.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   int dtype, void* stream);
 
 /*
  * Local (sliding-window) attention.  The tiled forward of "01 · IO-awareness、

@@ -36,7 +36,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
     assert set(syms) == {"fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
-                         "fa_bwd_workspace_bytes", "fa_fwd_window", "fa_bwd_window",
+                         "fa_bwd_workspace_bytes", "fa_bwd_noalloc", "fa_fwd_window", "fa_bwd_window",
                          "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes",
                          "fa_strerror"}
     for s in syms:
@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_codes():
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         msg = fa.fa_strerror(code)
         assert msg and msg != "unknown status", code
     assert fa.fa_strerror(-99) == "unknown status"
@@ -116,6 +116,29 @@ def test_bwd_validation_codes():
     need = fa.fa_bwd_workspace_bytes(1, 2, 32, 32, 64, fa.FA_BF16)
     assert bwd(workspace_bytes=need - 1) == -6
     assert bwd(B=0) == 0
+
+
+def bwd_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dO=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             B=1, H=2, Nq=32, Nk=32, d=64, scale=0.125, causal=1, dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_bwd_noalloc(**a)
+
+
+def test_bwd_noalloc_validation_codes():
+    # fa_bwd's own checks, before any HIP call
+    assert bwd_noalloc(dtype=fa.FA_F32) == -4
+    assert bwd_noalloc(d=32) == -3
+    assert bwd_noalloc(Nk=-1) == -2
+    assert bwd_noalloc(scale=float("nan")) == -8
+    assert bwd_noalloc(B=0, q=0, k=0, v=0, o=0, lse=0, dO=0, dq=0, dk=0, dv=0) == 0
+    # the static array holds two fp32 vectors of up to 2^20 query rows
+    limit = (8 << 20) // 8
+    assert fa.fa_bwd_workspace_bytes(8, 32, 4096, 4096, 128, fa.FA_BF16) == 8 << 20
+    assert 8 * 32 * 4096 == limit
+    assert bwd_noalloc(B=1, H=1, Nq=limit + 1, Nk=64) == -10
+    assert bwd_noalloc(B=3, H=32, Nq=limit // 96 + 64, Nk=64) == -10
+    assert "static buffer" in fa.fa_strerror(-10)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
