@@ -64,6 +64,24 @@ def visible_pairs(Nq: int, Nk: int, causal: bool, window=None) -> int:
     return total
 
 
+def atomic_adds(Nq: int, Nk: int, causal: bool, window, d: int) -> int:
+    """float32 atomic adds of one head in the backward's atomic mode: its
+    key-side kernel walks, for each 128-key tile, the 64-query steps that
+    can see it (as the kernel bounds them) and adds d values per query row
+    below Nq in every step."""
+    wl, wr = window if window is not None else ((None, 0) if causal else (None, None))
+    off = Nk - Nq
+    offr = None if wr is None else off + wr
+    offl = None if wl is None else off - wl
+    total = 0
+    for k0 in range(0, Nk, 128):
+        qstart = 0 if offr is None else max(0, k0 - offr)
+        qend = Nq if offl is None else max(0, min(Nq, k0 + 128 - offl))
+        for q0 in range(qstart // 64 * 64, qend, 64):
+            total += min(64, Nq - q0) * d
+    return total
+
+
 def fwd_flops(w) -> int:
     return 4 * w.d * visible_pairs(w.Nq, w.Nk, w.causal, w.window) * w.B * w.H
 
@@ -250,6 +268,34 @@ def mfma_probe(grid: int = 1024, iters: int = 4000, repeats: int = 3) -> dict:
             "tflops": round(tf, 1), "sclk_ghz": round(ghz, 3), "frac_of_published": round(tf / PEAK["bf16"], 4)}
 
 
+def atomic_probe(grid: int = 8192, repeats: int = 5) -> dict:
+    """Chip-wide rate of float32 buffer atomic adds to distinct addresses
+    (libfa_probe.so), the bound of the backward's atomic-dQ mode; median of
+    ``repeats`` launches."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_20_amd", "libfa_probe.so"))
+    lib.fa_probe_atomic_elems.restype = ctypes.c_long
+    lib.fa_probe_atomic_elems.argtypes = [ctypes.c_int]
+    lib.fa_probe_atomic_launch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    n = lib.fa_probe_atomic_elems(grid)
+    buf = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(repeats + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.fa_probe_atomic_launch(ctypes.c_void_p(buf.data_ptr()), grid, ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if st != 0:
+            raise RuntimeError(f"fa_probe_atomic_launch failed with {st}")
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts[1:])[repeats // 2]
+    return {"op": "libfa_probe: fp32 buffer atomic add, distinct addresses, 256 B per wave instruction",
+            "adds_per_s": round(n / (ms * 1e-3), -8), "ms": round(ms, 4), "adds": n}
+
+
 def time_launches(fn, stream, steps: int, warmup: int) -> float:
     """Average ms per call of ``fn`` with HIP events on ``stream``."""
     import torch
@@ -280,22 +326,15 @@ def train_step_timing(fa, wl, steps: int, warmup: int, window=None, w=None):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    need = fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     fwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                 w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), fa.FA_BF16, sh)
-    bwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), fa.FA_BF16,
-                ws.data_ptr(), need, sh)
-
     f_fwd, f_bwd = fa.fa_fwd, fa.fa_bwd
+    wa = None
     if window is not None:
         wa = tuple(-1 if x is None else x for x in window)
         fwd_args = fwd_args[:11] + wa + fwd_args[12:]
-        bwd_args = bwd_args[:15] + wa + bwd_args[16:]
         f_fwd, f_bwd = fa.fa_fwd_window, fa.fa_bwd_window
 
     def fwd():
@@ -303,23 +342,40 @@ def train_step_timing(fa, wl, steps: int, warmup: int, window=None, w=None):
         if st != 0:
             raise fa.FAError(st, f_fwd.__name__)
 
-    def bwd():
-        st = f_bwd(*bwd_args)
-        if st != 0:
-            raise fa.FAError(st, f_bwd.__name__)
+    def bwd_fn(det):
+        need = fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16, det)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        mask = (int(w.causal),) if wa is None else wa
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                w.B, w.H, w.Nq, w.Nk, w.d, w.scale) + mask + (fa.FA_BF16, det, ws.data_ptr(), need, sh)
+
+        def bwd():
+            st = f_bwd(*args)
+            if st != 0:
+                raise fa.FAError(st, f_bwd.__name__)
+        bwd.ws = ws
+        return bwd
 
     fwd()
     ms_f = time_launches(fwd, stream, steps, warmup)
-    ms_b = time_launches(bwd, stream, steps, warmup)
+    ms_b = time_launches(bwd_fn(1), stream, steps, warmup)
+    ms_a = time_launches(bwd_fn(0), stream, steps, warmup)
     causal = w.causal if window is None else False
     pairs = visible_pairs(w.Nq, w.Nk, causal, window) * w.B * w.H
     shape = w.describe() if window is None else w.describe().replace("causal", f"window {window}")
+    # the atomic mode's float32 adds: 64 x d per (64-query, 128-key) tile pair
+    atomics = atomic_adds(w.Nq, w.Nk, causal, window, w.d) * w.B * w.H
     return {"workload": w.name, "shape": shape,
             "fwd_ms": round(ms_f, 5), "fwd_tflops": round(4 * w.d * pairs / ms_f / 1e9, 3),
             "bwd_ms": round(ms_b, 5), "bwd_tflops": round(10 * w.d * pairs / ms_b / 1e9, 3),
+            "bwd_atomic_ms": round(ms_a, 5),
+            "bwd_atomic_tflops": round(10 * w.d * pairs / ms_a / 1e9, 3),
+            "bwd_atomic_adds": atomics,
             "bwd_flops": 10 * w.d * pairs,
-            "note": "bwd = dQ kernel (also D, LSE*log2e) + key-side kernel(s); 10*d FLOPs per "
-                    "visible pair"}
+            "note": "bwd = deterministic mode (dQ kernel + key-side kernel(s), the default); "
+                    "bwd_atomic = pre-pass, one key-side kernel adding dQ with fp32 atomics, dQ "
+                    "conversion; both counted at 10*d FLOPs per visible pair"}
 
 
 def gemm_ceiling(n: int = 8192, iters: int = 20) -> dict:
@@ -392,12 +448,12 @@ def bench_varlen(fa, wl, w, args) -> dict:
         g = torch.Generator(device="cpu").manual_seed(w.seed + 1)
         do = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-        need = fa.fa_bwd_varlen_workspace_bytes(w.H, T, w.d, fa.FA_BF16)
+        need = fa.fa_bwd_varlen_workspace_bytes(w.H, T, w.d, fa.FA_BF16, 0)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         step()
         bargv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()) + argv[5:17] + \
-                (fa.FA_BF16, ws.data_ptr(), need, stream.cuda_stream)
+                (fa.FA_BF16, 0, ws.data_ptr(), need, stream.cuda_stream)
 
         def bwd():
             st = fa.fa_bwd_varlen(*bargv)
@@ -407,7 +463,8 @@ def bench_varlen(fa, wl, w, args) -> dict:
         ms_b = time_launches(bwd, stream, 20, 5)
         result["backward"] = {"bwd_ms": round(ms_b, 5),
                               "bwd_tflops": round(10 * w.d * pairs * w.H / ms_b / 1e9, 3),
-                              "note": "fa_bwd_varlen: dQ (also D, LSE*log2e) + key side; 10*d FLOPs per visible pair"}
+                              "note": "fa_bwd_varlen, fast mode (pre-pass, key-side kernel with dQ "
+                                      "atomics, dQ conversion); 10*d FLOPs per visible pair"}
     if not args.no_cpu_baseline:
         from oracle import attention_forward
         # whole (head, sequence) pairs, head by head, until ~15 s of CPU work
@@ -664,7 +721,11 @@ def main():
         result["mfma_ceiling"] = gc
     if not args.no_train_step:
         tw = {x.name: x for x in wl.ALL}[args.train_workload]
-        result["train_step"] = train_step_timing(fa, wl, steps=20, warmup=5, w=tw)
+        ts = train_step_timing(fa, wl, steps=20, warmup=5, w=tw)
+        ap = atomic_probe()
+        ap["bwd_atomic_bound_ms"] = round(ts["bwd_atomic_adds"] / ap["adds_per_s"] * 1e3, 4)
+        ts["atomic_probe"] = ap
+        result["train_step"] = ts
         if w.window is not None:
             result["train_step_window"] = train_step_timing(fa, wl, steps=20, warmup=5,
                                                             window=(1023, 0))

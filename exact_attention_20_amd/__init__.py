@@ -11,21 +11,21 @@ Raw entry points, same names and argument order as ``include/fa.h``:
                    workspace, workspace_bytes, stream) -> int
     fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, n_splits) -> int
     fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal,
-           dtype, workspace, workspace_bytes, stream) -> int
-    fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) -> int
+           dtype, deterministic, workspace, workspace_bytes, stream) -> int
+    fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype, deterministic) -> int
     fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype,
                    stream) -> int
     fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, d, scale, window_left, window_right,
                   dtype, stream) -> int
     fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, window_left,
-                  window_right, dtype, workspace, workspace_bytes, stream) -> int
+                  window_right, dtype, deterministic, workspace, workspace_bytes, stream) -> int
     fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k,
                   max_seqlen_q, max_seqlen_k, d, scale, window_left, window_right, dtype,
                   stream) -> int
     fa_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, H,
                   total_q, total_k, max_seqlen_q, max_seqlen_k, d, scale, window_left,
-                  window_right, dtype, workspace, workspace_bytes, stream) -> int
-    fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype) -> int
+                  window_right, dtype, deterministic, workspace, workspace_bytes, stream) -> int
+    fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype, deterministic) -> int
     fa_strerror(status) -> str
 (pointer arguments are integers: device addresses, 0 for NULL)
 
@@ -33,13 +33,13 @@ Tensor helpers that allocate the outputs with torch and raise ``FAError`` on a
 non-zero status:
     attention_forward(q, k, v, scale=None, causal=False, window=None) -> (o, lse)
     attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0) -> (o, lse)
-    attention_backward(q, k, v, o, lse, do, scale=None, causal=False, window=None)
-        -> (dq, dk, dv)
+    attention_backward(q, k, v, o, lse, do, scale=None, causal=False, window=None,
+                       deterministic=True) -> (dq, dk, dv)
     attention_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                              max_seqlen_k, scale=None, causal=False, window=None) -> (o, lse)
     attention_backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                              max_seqlen_k, scale=None, causal=False, window=None)
-        -> (dq, dk, dv)
+                              max_seqlen_k, scale=None, causal=False, window=None,
+                              deterministic=True) -> (dq, dk, dv)
 ``window`` is a local window (wl, wr): key j is visible to query i iff
 i + (Nk - Nq) - wl <= j <= i + (Nk - Nq) + wr, a side None for no bound; it
 replaces ``causal`` (giving both raises ValueError).  The varlen helpers take
@@ -97,23 +97,23 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
-    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd_noalloc.restype = i
-    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
     lib.fa_fwd_window.restype = i
     lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i,
-                                  vp, sz, vp]
+                                  i, vp, sz, vp]
     lib.fa_bwd_window.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
-                                  f, i, i, i, vp, sz, vp]
+                                  f, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_varlen.restype = i
-    lib.fa_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_varlen_workspace_bytes.restype = sz
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
@@ -142,10 +142,11 @@ def fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, n_splits) -> int:
 
 
 def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype,
-           workspace, workspace_bytes, stream) -> int:
+           deterministic, workspace, workspace_bytes, stream) -> int:
     return load_library().fa_bwd(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq), _p(dk),
                                  _p(dv), B, H, Nq, Nk, d, float(scale), int(causal), int(dtype),
-                                 _p(workspace), int(workspace_bytes), _p(stream))
+                                 int(deterministic), _p(workspace), int(workspace_bytes),
+                                 _p(stream))
 
 
 def fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype,
@@ -155,8 +156,8 @@ def fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, caus
                                          int(dtype), _p(stream))
 
 
-def fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) -> int:
-    return int(load_library().fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype))
+def fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype, deterministic) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype, int(deterministic)))
 
 
 def fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, d, scale, window_left, window_right, dtype,
@@ -167,11 +168,12 @@ def fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, d, scale, window_left, window_r
 
 
 def fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, window_left,
-                  window_right, dtype, workspace, workspace_bytes, stream) -> int:
+                  window_right, dtype, deterministic, workspace, workspace_bytes, stream) -> int:
     return load_library().fa_bwd_window(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
                                         _p(dk), _p(dv), B, H, Nq, Nk, d, float(scale),
                                         int(window_left), int(window_right), int(dtype),
-                                        _p(workspace), int(workspace_bytes), _p(stream))
+                                        int(deterministic), _p(workspace), int(workspace_bytes),
+                                        _p(stream))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k,
@@ -185,17 +187,18 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, to
 
 def fa_bwd_varlen(q, k, v, o, lse, dO, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, H, total_q,
                   total_k, max_seqlen_q, max_seqlen_k, d, scale, window_left, window_right,
-                  dtype, workspace, workspace_bytes, stream) -> int:
+                  dtype, deterministic, workspace, workspace_bytes, stream) -> int:
     return load_library().fa_bwd_varlen(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
                                         _p(dk), _p(dv), _p(cu_seqlens_q), _p(cu_seqlens_k), B, H,
                                         total_q, total_k, max_seqlen_q, max_seqlen_k, d,
                                         float(scale), int(window_left), int(window_right),
-                                        int(dtype), _p(workspace), int(workspace_bytes),
-                                        _p(stream))
+                                        int(dtype), int(deterministic), _p(workspace),
+                                        int(workspace_bytes), _p(stream))
 
 
-def fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype) -> int:
-    return int(load_library().fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype))
+def fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype, deterministic) -> int:
+    return int(load_library().fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype,
+                                                             int(deterministic)))
 
 
 def fa_strerror(status: int) -> str:
@@ -319,10 +322,12 @@ def attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0, wor
 
 
 def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=None,
-                       window=None):
+                       window=None, deterministic=True):
     """dq, dk, dv of sum(do * o) via fa_bwd, or fa_bwd_window (bf16 only).
     ``o`` and ``lse`` are the outputs of ``attention_forward`` for the same
-    inputs and mask."""
+    inputs and mask.  ``deterministic`` (the default, and the faster mode on
+    MI355X) runs the bitwise-repeatable kernels; False runs the single
+    key-side kernel that sums dQ with fp32 atomics."""
     import torch
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
@@ -332,7 +337,7 @@ def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=
         _check(t, n, s, dt, q.device)
     _check(lse, "lse", (B, H, Nq), torch.float32, q.device)
     code = _dtype_code(q)
-    need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, code)
+    need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, code, deterministic)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -343,9 +348,11 @@ def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=
     ws = _ws_args(workspace, q.device)
     with torch.cuda.device(q.device):
         if w is None:
-            st = fa_bwd(*ptrs, B, H, Nq, Nk, d, scale, causal, code, *ws, _stream(q.device))
+            st = fa_bwd(*ptrs, B, H, Nq, Nk, d, scale, causal, code, deterministic, *ws,
+                        _stream(q.device))
         else:
-            st = fa_bwd_window(*ptrs, B, H, Nq, Nk, d, scale, w[0], w[1], code, *ws, _stream(q.device))
+            st = fa_bwd_window(*ptrs, B, H, Nq, Nk, d, scale, w[0], w[1], code, deterministic, *ws,
+                               _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_bwd" if w is None else "fa_bwd_window")
     return dq, dk, dv
@@ -407,9 +414,10 @@ def attention_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
 
 def attention_backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                               max_seqlen_k, scale=None, causal=False, window=None,
-                              workspace=None):
+                              workspace=None, deterministic=True):
     """dq, dk, dv of sum(do * o) for ``attention_forward_varlen`` via
-    fa_bwd_varlen (bf16); the same packing, offsets and mask as the forward."""
+    fa_bwd_varlen (bf16); the same packing, offsets and mask as the forward.
+    ``deterministic`` as in ``attention_backward``."""
     import torch
     H, Tq, d = q.shape
     Tk = k.shape[1]
@@ -421,7 +429,7 @@ def attention_backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, m
     _check_cu(cu_seqlens_q, "cu_seqlens_q", B, q.device)
     _check_cu(cu_seqlens_k, "cu_seqlens_k", B, q.device)
     code = _dtype_code(q)
-    need = fa_bwd_varlen_workspace_bytes(H, Tq, d, code)
+    need = fa_bwd_varlen_workspace_bytes(H, Tq, d, code, deterministic)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -432,7 +440,7 @@ def attention_backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, m
                            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Tq, Tk,
                            int(max_seqlen_q), int(max_seqlen_k), d, scale, wl, wr, code,
-                           *_ws_args(workspace, q.device), _stream(q.device))
+                           deterministic, *_ws_args(workspace, q.device), _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_bwd_varlen")
     return dq, dk, dv

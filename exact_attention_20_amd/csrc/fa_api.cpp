@@ -189,12 +189,22 @@ int fa::bwd_check_args(const void* q, const void* k, const void* v, const void* 
     return FA_OK;
 }
 
-extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
+namespace {
+
+// The backward workspace over `rows` query rows: LSE2 and D (float32 row
+// vectors), and in the atomic mode the float32 dQ buffer [rows, d]; each part
+// rounded up to 256 bytes.
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+size_t bwd_ws_bytes(size_t rows, int d, int deterministic) {
+    return 2 * round256(rows * sizeof(float)) + (deterministic ? 0 : round256(rows * d * sizeof(float)));
+}
+
+}  // namespace
+
+extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int deterministic) {
     if (check_common(B, H, Nq, Nk, d, 1.0f, dtype) != FA_OK) return 0;
     if (dtype != FA_BF16) return 0;
-    const size_t rows = (size_t)B * H * Nq;
-    const size_t vec = (rows * sizeof(float) + 255) & ~(size_t)255;
-    return 2 * vec;
+    return bwd_ws_bytes((size_t)B * H * Nq, d, deterministic);
 }
 
 namespace {
@@ -202,17 +212,17 @@ namespace {
 int bwd_impl(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dO, void* dq, void* dk, void* dv,
              int B, int H, int Nq, int Nk, int d, float scale, Mask mask,
-             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+             int dtype, int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
     bool work = false;
     int st = fa::bwd_check_args(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, dtype, &work);
     if (st != FA_OK || !work) return st;
     const long BH = (long)B * H;
-    const size_t need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype);
+    const size_t need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype, deterministic);
     if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
 
     const size_t rows = (size_t)BH * Nq;
-    const size_t vec_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
+    const size_t vec_bytes = round256(rows * sizeof(float));
     fa::BwdParams p = {};
     p.q = q;
     p.k = k;
@@ -225,6 +235,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o,
     p.dv = dv;
     p.lse2 = (float*)workspace;
     p.dvec = (float*)((char*)workspace + vec_bytes);
+    p.dqacc = deterministic ? nullptr : (float*)((char*)workspace + 2 * vec_bytes);
     p.Nq = Nq;
     p.Nk = Nk;
     p.BH = (int)BH;
@@ -238,7 +249,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o,
     p.scale_log2 = scale * 1.44269504088896340736f;
     p.wl = mask.wl;
     p.wr = mask.wr;
-    return hip_status(fa::launch_bwd(d, mask.mode, false, p, (hipStream_t)stream));
+    if (deterministic) return hip_status(fa::launch_bwd(d, mask.mode, false, p, (hipStream_t)stream));
+    return hip_status(fa::launch_bwd_atomic(d, mask.mode, false, p, (long)rows, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -261,21 +273,22 @@ extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* 
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dO, void* dq, void* dk, void* dv,
                       int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                      int dtype, int deterministic, void* workspace, size_t workspace_bytes,
+                      void* stream) {
     return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal_mask(causal),
-                    dtype, workspace, workspace_bytes, stream);
+                    dtype, deterministic, workspace, workspace_bytes, stream);
 }
 
 extern "C" int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dO, void* dq, void* dk, void* dv,
                              int B, int H, int Nq, int Nk, int d, float scale,
-                             int window_left, int window_right, int dtype,
+                             int window_left, int window_right, int dtype, int deterministic,
                              void* workspace, size_t workspace_bytes, void* stream) {
     Mask m;
     const int st = window_mask(window_left, window_right, &m);
     if (st != FA_OK) return st;
-    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, m, dtype, workspace,
-                    workspace_bytes, stream);
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, m, dtype, deterministic,
+                    workspace, workspace_bytes, stream);
 }
 
 namespace {
@@ -351,13 +364,11 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
     return hip_status(fa::launch_fwd_varlen(d, m.mode, p, (hipStream_t)stream));
 }
 
-extern "C" size_t fa_bwd_varlen_workspace_bytes(int H, int total_q, int d, int dtype) {
-    // the same two row vectors as fa_bwd's, over the H * total_q packed rows
+extern "C" size_t fa_bwd_varlen_workspace_bytes(int H, int total_q, int d, int dtype, int deterministic) {
+    // fa_bwd's workspace over the H * total_q packed rows
     if (H < 0 || total_q < 0 || (d != 64 && d != 128) || dtype != FA_BF16) return 0;
     if ((long double)H * total_q > 2.0e11L) return 0;
-    const size_t rows = (size_t)H * total_q;
-    const size_t vec = (rows * sizeof(float) + 255) & ~(size_t)255;
-    return 2 * vec;
+    return bwd_ws_bytes((size_t)H * total_q, d, deterministic);
 }
 
 extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
@@ -365,7 +376,7 @@ extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const 
                              const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
                              int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
                              float scale, int window_left, int window_right, int dtype,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
     Mask m;
     int st = window_mask(window_left, window_right, &m);
     if (st != FA_OK) return st;
@@ -379,12 +390,12 @@ extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const 
     if (has_q && (!aligned16(q) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) || !aligned4(lse)))
         return FA_ERR_ALIGN;
     if (has_k && (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))) return FA_ERR_ALIGN;
-    const size_t need = fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype);
+    const size_t need = fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype, deterministic);
     if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
 
     const size_t rows = (size_t)H * total_q;
-    const size_t vec_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
+    const size_t vec_bytes = round256(rows * sizeof(float));
     fa::BwdParams p = {};
     p.q = q;
     p.k = k;
@@ -397,6 +408,7 @@ extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const 
     p.dv = dv;
     p.lse2 = (float*)workspace;
     p.dvec = (float*)((char*)workspace + vec_bytes);
+    p.dqacc = deterministic ? nullptr : (float*)((char*)workspace + 2 * vec_bytes);
     p.BH = (int)((long)B * H);
     // workgroups per (batch, head): tiles of the longest sequence, unpaired
     p.kv_slots = (max_seqlen_k + 127) / 128;
@@ -408,7 +420,8 @@ extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const 
     p.wl = m.wl;
     p.wr = m.wr;
     p.vl = varlen_params(cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q, max_seqlen_k);
-    return hip_status(fa::launch_bwd(d, m.mode, true, p, (hipStream_t)stream));
+    if (deterministic) return hip_status(fa::launch_bwd(d, m.mode, true, p, (hipStream_t)stream));
+    return hip_status(fa::launch_bwd_atomic(d, m.mode, true, p, (long)rows, (hipStream_t)stream));
 }
 
 extern "C" const char* fa_strerror(int status) {

@@ -551,6 +551,423 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// 4. Atomic mode: one key-side kernel for dV, dK and dQ.  The walk is that of
+// bwd_dkdv_kernel (one workgroup per (batch*head, 128-key tile), 64-query
+// steps); each step also forms the tile's share of dQ, dS K over its 128
+// keys, and adds it to an fp32 dQ buffer with atomics, so every visible
+// (query, key) pair costs the 5 products of the loop in §5: S, dP, dV, dK
+// and dQ (the dQ "needs atomic adds or a separate reduction" remark there).
+//
+// QSPLIT waves share each 32-key slice: wave w owns keys 32*(w%4) .. +31 of
+// the tile and queries (w/4)*WQ .. +WQ-1 of every step (WQ = 64 / QSPLIT).
+// At d = 128 this keeps dK, dV, S, dP and the dQ block within 256 registers
+// (two waves per SIMD, eight-wave workgroups); the slice's partial dK and dV
+// are summed through LDS at the end of the walk.  At d = 64, QSPLIT = 1.
+//
+// Each step: S, dP, P, dS as in bwd_dkdv_kernel; dS (bf16) goes to an LDS
+// tile [128 keys][64 queries]; dV^T += dO^T P and dK^T += Q^T dS; barrier;
+// then wave w forms one 32x32 block of the step's dQ (query block w / NDB,
+// head-dim block w % NDB) as dS K over the 128 keys -- A = dS read
+// transposed from the dS tile, B = K read transposed from a K tile kept in
+// LDS for the whole walk -- and adds its 16 values per lane to the fp32 dQ
+// buffer with buffer atomics (rows past Nq fall outside the buffer range and
+// are dropped by the hardware).
+//
+// The atomics are issued after the next stage's copies and are left in
+// flight across the end-of-step barrier: vector memory operations of a wave
+// complete in issue order, so waiting until no more than kAtomics are
+// outstanding waits for the copies (and the previous steps' atomics) only.
+//
+// Cost: one float32 atomic add per (query row, head-dim column, 128-key
+// tile), 64 x d per step, and MI355X retires about 3.2e11 such adds per
+// second chip-wide (buffer atomics to distinct addresses, measured), a
+// quarter of its plain-store rate.  That bounds this kernel well above the
+// two deterministic kernels' time (0.87 vs 0.52 ms at B=4 H=16 N=4096 d=64
+// causal), which is why the deterministic mode is the default.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void vmem_wait_n() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    // vmcnt bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15) not waited on
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+template <int D, int MASK, bool VARLEN = false, int QSPLIT = 1>
+__global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1) bwd_fused_kernel(BwdParams p) {
+    constexpr int NW = 4 * QSPLIT;
+    constexpr int BKV = 128, BQ = 64, WQ = BQ / QSPLIT;
+    constexpr int NQB = WQ / 32;              // 32-query blocks per wave and step
+    constexpr int NQC = WQ / 16;              // 16-query k-steps
+    constexpr int NKK = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int DQB = 2 * NDB / NW;         // 32x32 dQ blocks per wave (same query block)
+    static_assert(DQB >= 1 && DQB * NW == 2 * NDB && NDB % DQB == 0, "dQ blocks split evenly");
+    constexpr int T_BYTES = BQ * D * 2;
+    constexpr int V_OFF = 2 * T_BYTES;
+    constexpr int STAGE = V_OFF + 2 * BQ * 4;
+    constexpr int K_OFF = 2 * STAGE;          // K tile [BKV][D], resident for the walk
+    constexpr int DS_OFF = K_OFF + BKV * D * 2;   // dS^T tile [BKV][BQ]
+    constexpr int SMEM = DS_OFF + BKV * BQ * 2;
+    static_assert(K_OFF % 1024 == 0 && DS_OFF % 1024 == 0, "tiles start on 1 KiB");
+    static_assert(QSPLIT == 1 || 4 * NDB * 16 * 64 * 4 <= SMEM, "room for the partial dK / dV");
+    constexpr int kAtomics = 16 * DQB;        // its fp32 dQ values per lane and step
+    // d = 128: K's B operand of S is read from the K tile instead of held in
+    // 32 registers (the kernel would spill otherwise)
+    constexpr bool kKRegs = D == 64 || QSPLIT == 1;
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hg = lane >> 5;
+    const int wk = wave & 3, wq = wave >> 2;  // key slice, query part
+    const int qw0 = wq * WQ;                  // this wave's first query of a step
+    const int dq_qb = wave * DQB / NDB, dq_db = wave * DQB % NDB;   // its first dQ block
+    int bh, slot;
+    if (VARLEN) varlen_slot(p.vl, p.kv_slots, blockIdx.x, bh, slot);
+    else map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, slot);
+    SeqGeometry sg;
+    if constexpr (VARLEN) sg = seq_geometry(p.vl, bh);
+    else sg = SeqGeometry{p.Nq, p.Nk, (size_t)bh * p.Nq, (size_t)bh * p.Nk};
+    const int Nq = sg.Nq, Nk = sg.Nk, off = Nk - Nq;
+    constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
+    const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
+    const int offl = off - (MASK == kMaskWindow ? p.wl : 0);
+    const int n_kt = (Nk + BKV - 1) / BKV;
+    if (VARLEN && slot >= n_kt) return;
+    const int n_items = (p.kv_paired && slot != n_kt - 1 - slot) ? 2 : 1;
+
+    const bf16* Qh = (const bf16*)p.q + sg.q_row0 * D;
+    const bf16* Kh = (const bf16*)p.k + sg.k_row0 * D;
+    const bf16* Vh = (const bf16*)p.v + sg.k_row0 * D;
+    const bf16* dOh = (const bf16*)p.dO + sg.q_row0 * D;
+    float* dQa = p.dqacc + sg.q_row0 * D;
+
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (uint32_t)Nk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, (uint32_t)Nk * D * 2);
+    const TileCopy<D, BQ, NW> copier(wave, lane);
+    const TileCopy<D, BKV, NW> kcopier(wave, lane);
+    const i32x4 rq_w = make_rsrc_words(Qh, (uint32_t)Nq * D * 2);
+    const i32x4 rdo_w = make_rsrc_words(dOh, (uint32_t)Nq * D * 2);
+    const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
+    const uint32_t smem_lds = lds_address(smem);
+    const char* ktile = smem + K_OFF;
+    char* dstile = smem + DS_OFF;
+
+    // this lane's byte offsets of its dQ block items in a step's rows:
+    // item 4g+e is query 32*dq_qb + 8g + 4hg + e, column 32*dq_db + l32
+    const uint32_t dq_off0 = (uint32_t)(((dq_qb * 32 + 4 * hg) * D + dq_db * 32 + l32) * 4);
+
+    for (int it = 0; it < n_items; ++it) {
+    const int kt = it == 0 ? slot : n_kt - 1 - slot;
+    const int k0 = kt * BKV;
+    const int kw = k0 + wk * 32;              // this wave's first key
+    const int kj = kw + l32;                  // this lane's key
+
+    // K^T (unless read from the K tile) and V^T as B operands: lane = key
+    bf16x8 kreg[kKRegs ? NKK : 1], vreg[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const uint32_t o = (uint32_t)kj * D * 2 + (16 * kk + 8 * hg) * 2;
+        if constexpr (kKRegs) kreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rk, o, 0));
+        vreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rv, o, 0));
+    }
+
+    const int qstart = kRight ? max(0, k0 - offr) : 0;
+    const int qt0 = qstart / BQ;
+    const int qend = kLeft ? max(0, min(Nq, k0 + BKV - offl)) : Nq;
+    const int n_qt = (qend + BQ - 1) / BQ;
+    const int wq_first = kRight ? kw - offr : 0;
+    const int wq_last = kLeft ? kw + 31 - offl : Nq;
+
+    auto load_step = [&](int qt, int stage) {
+        const uint32_t base = smem_lds + stage * STAGE;
+        copier.issue(rq_w, qt * BQ, base);
+        copier.issue(rdo_w, qt * BQ, base + T_BYTES);
+    };
+    const float* L2h = p.lse2 + sg.q_row0;
+    const float* Dh = p.dvec + sg.q_row0;
+    float nl2 = INFINITY, ndd = 0.f;
+    auto fetch_vec = [&](int qt) {
+        const int q = qt * BQ + lane;
+        nl2 = q < Nq ? L2h[q] : INFINITY;
+        ndd = q < Nq ? Dh[q] : 0.f;
+    };
+    auto store_vec = [&](int stage) {
+        float* v = (float*)(smem + stage * STAGE + V_OFF);
+        v[lane] = nl2;
+        v[BQ + lane] = ndd;
+    };
+
+    f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        dkacc[db] = zero16();
+        dvacc[db] = zero16();
+    }
+
+    kcopier.issue(rk_w, k0, smem_lds + K_OFF);
+    if (qt0 < n_qt) {
+        load_step(qt0, 0);
+        if (wave == 0) {
+            fetch_vec(qt0);
+            store_vec(0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    tile_barrier();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        if constexpr (kKRegs) mark_loaded(kreg[kk]);
+        mark_loaded(vreg[kk]);
+    }
+
+    for (int qt = qt0; qt < n_qt; ++qt) {
+        const int st = (qt - qt0) & 1;
+        const char* qs = smem + st * STAGE;
+        const char* dos = qs + T_BYTES;
+        const float* l2s = (const float*)(qs + V_OFF);
+        const float* dds = l2s + BQ;
+        const int q0 = qt * BQ;
+        const int qa = q0 + qw0;              // this wave's first query
+        const bool has_next = qt + 1 < n_qt;
+        if (has_next) {
+            load_step(qt + 1, st ^ 1);
+            if (wave == 0) fetch_vec(qt + 1);
+        }
+
+        const bool active = kw < Nk && qa + WQ - 1 >= wq_first && (!kLeft || qa <= wq_last);
+        if (active) {
+            // ---- S = Q K^T and dP = dO V^T (lane = key, items = queries) ----
+            f32x16 s[NQB], dp[NQB];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                s[qb] = zero16();
+                dp[qb] = zero16();
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    const bf16x8 kb = kKRegs ? kreg[kKRegs ? kk : 0] : tile_read_row<D>(ktile, wk * 32, kk, lane);
+                    s[qb] = mfma_bf16(tile_read_row<D>(qs, qw0 + qb * 32, kk, lane), kb, s[qb]);
+                    dp[qb] = mfma_bf16(tile_read_row<D>(dos, qw0 + qb * 32, kk, lane), vreg[kk], dp[qb]);
+                }
+            if constexpr (D == 128 && NQB == 1 && !kKRegs) {
+                // the three operand reads of a k-step (Q, dO, K) two k-steps
+                // ahead of its two MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    if (kk + 2 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                }
+            }
+            // ---- mask: steps that straddle a bound, the query tail or the
+            // key tail (keys past Nk: P = 0, so dS stays finite) ----
+            const bool need_mask = (qa + WQ > Nq) || (kw + 31 >= Nk) || (kRight && qa + offr < kw + 31) ||
+                                   (kLeft && qa + WQ - 1 + offl > kw);
+            if (need_mask) {
+                const int qb0 = qa + 4 * hg;
+                const int lo = kRight ? kj - offr - qb0 : -(1 << 30);
+                int hi = kj < Nk ? Nq - 1 - qb0 : -(1 << 30);
+                if (kLeft) hi = min(hi, kj - offl - qb0);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int o = qb * 32 + (i >> 2) * 8 + (i & 3);
+                        if (o < lo || o > hi) s[qb][i] = -INFINITY;
+                    }
+            }
+            u32x4 pw[NQC], dsw[NQC];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                float pv[16], dsv[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int ql = qw0 + qb * 32 + g * 8 + 4 * hg;
+                    const f32x4 l2 = *(const f32x4*)(l2s + ql);
+                    const f32x4 dd = *(const f32x4*)(dds + ql);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float pe = exp2_hw(fmaf(s[qb][4 * g + e], p.scale_log2, -l2[e]));
+                        pv[4 * g + e] = pe;
+                        dsv[4 * g + e] = pe * (dp[qb][4 * g + e] - dd[e]);
+                    }
+                }
+                pack_pairs(pv, pw[2 * qb], pw[2 * qb + 1]);
+                pack_pairs(dsv, dsw[2 * qb], dsw[2 * qb + 1]);
+            }
+            // ---- dS^T into the dS tile: k-step qc holds queries
+            // qc*16 + 4hg + {0..3} (words 0, 1) and qc*16 + 8 + 4hg + {0..3} ----
+            const uint32_t krow = (uint32_t)(wk * 32 + l32);
+#pragma unroll
+            for (int qc = 0; qc < NQC; ++qc) {
+                const uint32_t ch = (uint32_t)(qw0 / 8 + 2 * qc);
+                u32x2 a, b;
+                a[0] = dsw[qc][0];
+                a[1] = dsw[qc][1];
+                b[0] = dsw[qc][2];
+                b[1] = dsw[qc][3];
+                *(u32x2*)(dstile + tile_offset<BQ>(krow, ch) + 8 * hg) = a;
+                *(u32x2*)(dstile + tile_offset<BQ>(krow, ch + 1) + 8 * hg) = b;
+            }
+            // ---- dV^T += dO^T P ;  dK^T += Q^T dS ----
+#pragma unroll
+            for (int qc = 0; qc < NQC; ++qc)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qw0 + qc * 16, db * 32, lane),
+                                          __builtin_bit_cast(bf16x8, pw[qc]), dvacc[db]);
+                    dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qw0 + qc * 16, db * 32, lane),
+                                          __builtin_bit_cast(bf16x8, dsw[qc]), dkacc[db]);
+                }
+            if constexpr (D == 128) {   // two transposed reads per MFMA, four ahead
+                constexpr int nm = 2 * NQC * NDB;
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+                for (int i = 0; i < nm; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                    if (i < nm - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+                }
+            }
+        } else {
+            // no visible pair for this wave: its part of the dS tile is zero
+            const uint32_t krow = (uint32_t)(wk * 32 + l32);
+            u32x2 z;
+            z[0] = z[1] = 0u;
+#pragma unroll
+            for (int qc = 0; qc < NQC; ++qc) {
+                const uint32_t ch = (uint32_t)(qw0 / 8 + 2 * qc);
+                *(u32x2*)(dstile + tile_offset<BQ>(krow, ch) + 8 * hg) = z;
+                *(u32x2*)(dstile + tile_offset<BQ>(krow, ch + 1) + 8 * hg) = z;
+            }
+        }
+        tile_barrier();   // the whole dS tile is written
+
+        // ---- dQ block += dS K over the tile's 128 keys, added to the fp32
+        // buffer (rows q0 .. q0+63; rows past Nq are outside the range) ----
+        {
+            f32x16 dq[DQB];
+#pragma unroll
+            for (int b = 0; b < DQB; ++b) dq[b] = zero16();
+#pragma unroll
+            for (int kc = 0; kc < BKV / 16; ++kc) {
+                const bf16x8 a = tile_read_tr<BQ>(dstile, kc * 16, dq_qb * 32, lane);
+#pragma unroll
+                for (int b = 0; b < DQB; ++b)
+                    dq[b] = mfma_bf16(a, tile_read_tr<D>(ktile, kc * 16, (dq_db + b) * 32, lane), dq[b]);
+            }
+            const __amdgpu_buffer_rsrc_t rdq =
+                make_rsrc(dQa + (size_t)q0 * D, (uint32_t)(min(BQ, Nq - q0) * D * 4));
+            // row group g of the block through the scalar offset, the rest
+            // in the instruction's immediate: one offset register in all
+#pragma unroll
+            for (int b = 0; b < DQB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t o = dq_off0 + (uint32_t)(((i & 3) * D + 32 * b) * 4);
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[b][i], rdq, o, (i >> 2) * 8 * D * 4, 0);
+                }
+        }
+
+        if (has_next) {
+            if (wave == 0) store_vec(st ^ 1);
+            vmem_wait_n<kAtomics>();   // the next stage's copies landed; atomics may still fly
+        }
+        mark_loaded(nl2);
+        mark_loaded(ndd);
+        tile_barrier();
+    }
+
+    // ---- QSPLIT > 1: sum the slice's partial dK^T, dV^T through LDS (the
+    // stages, K and dS tiles are free after the walk) ----
+    if constexpr (QSPLIT > 1) {
+        float* red = (float*)smem + wk * (NDB * 16 * 64);
+        auto reduce = [&](f32x16 (&acc)[NDB]) {
+            if (wq != 0) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) red[(db * 16 + i) * 64 + lane] = acc[db][i];
+            }
+            tile_barrier();
+            if (wq == 0) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[db][i] += red[(db * 16 + i) * 64 + lane];
+            }
+            tile_barrier();
+        };
+        reduce(dkacc);
+        reduce(dvacc);
+    }
+
+    // ---- dK = scale * dK^T, dV = dV^T (lane = key, items = d) ----
+    if (wq == 0 && kj < Nk) {
+        bf16* dKr = (bf16*)p.dk + sg.k_row0 * D + (size_t)kj * D;
+        bf16* dVr = (bf16*)p.dv + sg.k_row0 * D + (size_t)kj * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int dcol = db * 32 + g * 8 + 4 * hg;
+                u32x2 wk2, wv;
+                wk2[0] = pack_bf16x2(dkacc[db][4 * g] * p.scale, dkacc[db][4 * g + 1] * p.scale);
+                wk2[1] = pack_bf16x2(dkacc[db][4 * g + 2] * p.scale, dkacc[db][4 * g + 3] * p.scale);
+                *(u32x2*)(dKr + dcol) = wk2;
+                wv[0] = pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]);
+                wv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
+                *(u32x2*)(dVr + dcol) = wv;
+            }
+    }
+    }   // items
+}
+
+// Atomic mode, before the fused kernel: for every query row, D = rowsum(dO * O)
+// and LSE * log2(e) (+inf for a row with no visible key) into the workspace,
+// and the row of the fp32 dQ buffer set to zero.  D / 8 lanes per row, 16
+// bytes each.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, long rows) {
+    constexpr int TPR = D / 8, RPB = 256 / TPR;
+    const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c = threadIdx.x % TPR;
+    if (row >= rows) return;   // whole rows leave together
+    const size_t e0 = (size_t)row * D + 8 * c;
+    const u32x4 a = ldg128((const bf16*)p.dO + e0), b = ldg128((const bf16*)p.o + e0);
+    float dd = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dd += bf16_lo(a[i]) * bf16_lo(b[i]) + bf16_hi(a[i]) * bf16_hi(b[i]);
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) dd += __shfl_xor(dd, m, TPR);
+    if (c == 0) {
+        const float lse = p.lse[row];
+        p.lse2[row] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+        p.dvec[row] = dd;
+    }
+    f32x4 z;
+    z[0] = z[1] = z[2] = z[3] = 0.f;
+    *(f32x4*)(p.dqacc + e0) = z;
+    *(f32x4*)(p.dqacc + e0 + 4) = z;
+}
+
+// Atomic mode, after the fused kernel: dQ = scale * (fp32 buffer), rounded to
+// bf16; 8 elements per lane.
+__global__ void __launch_bounds__(256) bwd_dq_convert_kernel(const float* acc, bf16* dq, float scale,
+                                                             size_t n8) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const f32x4 a = *(const f32x4*)(acc + 8 * i), b = *(const f32x4*)(acc + 8 * i + 4);
+    u32x4 w;
+    w[0] = pack_bf16x2(a[0] * scale, a[1] * scale);
+    w[1] = pack_bf16x2(a[2] * scale, a[3] * scale);
+    w[2] = pack_bf16x2(b[0] * scale, b[1] * scale);
+    w[3] = pack_bf16x2(b[2] * scale, b[3] * scale);
+    *(u32x4*)(dq + 8 * i) = w;
+}
+
+// ---------------------------------------------------------------------------
 // part: -1 the dQ kernel, 0/1/2 the key-side kernel's PART
 template <int D, int MASK, bool VARLEN>
 static const void* bwd_kernel_m(int part) {
@@ -601,8 +1018,58 @@ bool bwd_pair_tiles(bool causal, long bh, int n_tiles) {
     return causal && n_tiles >= 2 && n_tiles <= 64 && bh * n_tiles >= 4 * 512;
 }
 
+template <int D, bool VARLEN>
+static const void* bwd_fused(int mask) {
+#ifndef FA_BWD128_QSPLIT
+#define FA_BWD128_QSPLIT 2
+#endif
+    constexpr int QS = D == 64 ? 1 : FA_BWD128_QSPLIT;
+    if (mask == kMaskCausal) return (const void*)bwd_fused_kernel<D, kMaskCausal, VARLEN, QS>;
+    if (mask == kMaskWindow) return (const void*)bwd_fused_kernel<D, kMaskWindow, VARLEN, QS>;
+    return (const void*)bwd_fused_kernel<D, kMaskNone, VARLEN, QS>;
+}
+
+// Atomic mode: pre-pass (D, LSE2, dQ buffer = 0), the fused key-side
+// kernel, then dQ = scale * buffer in bf16.
+template <int D>
+static hipError_t launch_bwd_atomic_d(int mask, bool varlen, const BwdParams& p, long rows, hipStream_t s) {
+    BwdParams pp = p;
+    if (rows > 0) {
+        constexpr int RPB = 256 / (D / 8);
+        long rr = rows;
+        void* args[] = {&pp, &rr};
+        hipError_t e = hipLaunchKernel((const void*)bwd_prep_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)),
+                                       dim3(256), args, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    const long grid_kv = (long)p.BH * p.kv_slots;
+    if (grid_kv > 0) {
+        void* args[] = {&pp};
+        const void* fn = varlen ? bwd_fused<D, true>(mask) : bwd_fused<D, false>(mask);
+        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(D == 64 ? 256 : 256 * FA_BWD128_QSPLIT),
+                                       args, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    if (rows > 0) {
+        const float* acc = p.dqacc;
+        bf16* dq = (bf16*)p.dq;
+        float scale = p.scale;
+        size_t n8 = (size_t)rows * D / 8;
+        void* args[] = {&acc, &dq, &scale, &n8};
+        hipError_t e = hipLaunchKernel((const void*)bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)),
+                                       dim3(256), args, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_bwd(int d, int mask, bool varlen, BwdParams p, hipStream_t stream) {
     return d == 64 ? launch_bwd_d<64>(mask, varlen, p, stream) : launch_bwd_d<128>(mask, varlen, p, stream);
+}
+
+hipError_t launch_bwd_atomic(int d, int mask, bool varlen, BwdParams p, long rows, hipStream_t stream) {
+    return d == 64 ? launch_bwd_atomic_d<64>(mask, varlen, p, rows, stream)
+                   : launch_bwd_atomic_d<128>(mask, varlen, p, rows, stream);
 }
 
 }  // namespace fa

@@ -71,6 +71,7 @@ struct BwdParams {
     void* dv;
     float* lse2;       // [B,H,Nq] float32 workspace: LSE * log2(e), +inf for empty rows
     float* dvec;       // [B,H,Nq] float32 workspace: rowsum(dO * O)
+    float* dqacc;      // [B,H,Nq,d] float32 workspace of the atomic mode: dQ / scale
     int Nq;
     int Nk;
     int BH;
@@ -108,5 +109,9 @@ hipError_t launch_fwd_split(int d, bool causal, FwdParams p, hipStream_t stream)
 // varlen: the kernels take each (batch, head)'s geometry from p.vl; the
 // row-wise pre-pass covers all H * total_q packed rows.
 hipError_t launch_bwd(int d, int mask, bool varlen, BwdParams p, hipStream_t stream);
+// The atomic-dQ (non-deterministic) backward: a pre-pass over the `rows`
+// query rows, one key-side kernel adding dQ into p.dqacc with atomics, and
+// the dQ conversion.
+hipError_t launch_bwd_atomic(int d, int mask, bool varlen, BwdParams p, long rows, hipStream_t stream);
 
 }  // namespace fa

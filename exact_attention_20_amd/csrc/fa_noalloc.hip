@@ -1,5 +1,6 @@
-// fa_bwd_noalloc (include/fa.h): fa_bwd with its workspace in a static device
-// array instead of caller memory, for callers that cannot allocate.
+// fa_bwd_noalloc (include/fa.h): fa_bwd in its deterministic mode with the
+// workspace in a static device array instead of caller memory, for callers
+// that cannot allocate.
 //
 // The backward's workspace holds two float32 row vectors (the LSE in base-2
 // units and D = rowsum(dO * O)); the dQ kernel writes both for every query
@@ -46,11 +47,11 @@ extern "C" int fa_bwd_noalloc(const void* q, const void* k, const void* v, const
     bool work = false;
     const int chk = fa::bwd_check_args(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, dtype, &work);
     if (chk != FA_OK || !work) return chk;
-    if (fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype) > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+    if (fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype, 1) > (size_t)FA_NOALLOC_SCRATCH_BYTES)
         return FA_ERR_SCRATCH;
     void* ws = nullptr;
     const int st = scratch_of_current_device(&ws);
     if (st != FA_OK) return st;
-    return fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype, ws,
+    return fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype, 1, ws,
                   (size_t)FA_NOALLOC_SCRATCH_BYTES, stream);
 }

@@ -1,7 +1,9 @@
-// MFMA throughput probe (libfa_probe.so): the rate the bf16 matrix cores
-// sustain on this GPU under a pure MFMA load, and the core clock while they
-// do.  bench.py reports it beside the published 2.5 PFLOP/s peak as a
-// measured denominator.  Not part of the attention library.
+// Throughput probes (libfa_probe.so), not part of the attention library:
+//   * the rate the bf16 matrix cores sustain on this GPU under a pure MFMA
+//     load, and the core clock while they do -- bench.py reports it beside
+//     the published 2.5 PFLOP/s peak as a measured denominator;
+//   * the chip-wide rate of float32 buffer atomic adds to distinct
+//     addresses -- the bound of the backward's atomic-dQ mode.
 //
 // Each wave runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 on four
 // independent accumulator chains (no memory traffic inside the loop), so the
@@ -56,4 +58,29 @@ extern "C" int fa_probe_mfma_launch(void* out, void* clocks, int grid, int iters
 // FLOPs one launch executes: grid * 4 waves * iters * 16 MFMAs * 32768.
 extern "C" double fa_probe_mfma_flops(int grid, int iters) {
     return (double)grid * 4.0 * (double)iters * 16.0 * 32768.0;
+}
+
+// float32 atomic adds: each lane of workgroup w adds 1 to element
+// (w * ITERS + i) * 256 + threadIdx.x for i < ITERS, so every add of a
+// launch goes to its own address and a wave's 64 lanes to 256 contiguous
+// bytes.  `buf` holds grid * kAtomicIters * 256 floats.
+constexpr int kAtomicIters = 64;
+
+__global__ void __launch_bounds__(256) probe_atomic_kernel(float* buf, uint32_t n) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(buf, (short)0, n * 4u, 0x00020000);
+    for (int i = 0; i < kAtomicIters; ++i) {
+        const uint32_t idx = (blockIdx.x * kAtomicIters + i) * 256u + threadIdx.x;
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(1.0f, r, idx * 4u, 0, 0);
+    }
+}
+
+// buf: at least fa_probe_atomic_elems(grid) floats.  Returns 0, -1 for bad
+// arguments, -7 if the launch failed.
+extern "C" long fa_probe_atomic_elems(int grid) { return (long)grid * kAtomicIters * 256; }
+
+extern "C" int fa_probe_atomic_launch(void* buf, int grid, void* stream) {
+    if (!buf || grid <= 0 || fa_probe_atomic_elems(grid) * 4 > 0xffffffffL) return -1;
+    hipLaunchKernelGGL(probe_atomic_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (float*)buf,
+                       (uint32_t)fa_probe_atomic_elems(grid));
+    return hipGetLastError() == hipSuccess ? 0 : -7;
 }

@@ -125,11 +125,12 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes: two float32 row
- * vectors [B,H,Nq] (the LSE in base-2 units and D = rowsum(dO * O)), each
+ * Bytes of device workspace fa_bwd needs for these sizes and mode: two
+ * float32 row vectors [B,H,Nq] (the LSE in base-2 units and D = rowsum(dO *
+ * O)) and, unless `deterministic`, a float32 dQ buffer [B,H,Nq,d]; each part
  * rounded up to 256 bytes.  Returns 0 for invalid sizes or dtype.
  */
-size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int deterministic);
 
 /*
  * Backward pass by recomputation ("01 · IO-awareness、online softmax 与
@@ -141,28 +142,50 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
  *
  *   in : q, k, v, o (the forward output), lse (the forward LSE), dO
  *   out: dq [B,H,Nq,d], dk [B,H,Nk,d], dv [B,H,Nk,d]           (dtype)
- *   workspace: device memory of at least fa_bwd_workspace_bytes(); its
- *   contents on entry are ignored and on exit are unspecified.
+ *   workspace: device memory of at least fa_bwd_workspace_bytes() for the
+ *   same sizes and mode; its contents on entry are ignored and on exit are
+ *   unspecified.
  *
- * Only FA_BF16 is accepted (FA_ERR_DTYPE otherwise).  Deterministic: each
- * of dq, dk and dv is accumulated in registers by one workgroup, so the same
- * inputs give bitwise the same outputs.  Calls that share a workspace must
- * not overlap.
+ * The loop of §5 fixes a key block and walks the query blocks that see it,
+ * so dK and dV of a block are finished in one place while dQ is summed over
+ * key blocks, which takes atomic adds or a separate reduction; whether that
+ * sum is reproducible is the `deterministic` choice (the same section):
+ *   deterministic != 0 dQ is accumulated in registers by a second kernel per
+ *                      query tile, which computes S and dP again (7 products
+ *                      per visible (query, key) pair at d = 64, 8 at
+ *                      d = 128); every output is bitwise repeatable.  The
+ *                      faster mode on MI355X, and the one to use.
+ *   deterministic = 0  one kernel per key tile computes S, dP, dS, dV, dK and
+ *                      dS K (5 products per pair) and adds dS K into the
+ *                      float32 dQ buffer with atomics.  dK and dV are bitwise
+ *                      repeatable; dQ's float32 sum runs in whatever order
+ *                      the atomics land, so its bf16 rounding can differ
+ *                      between calls.  Its 64 x d atomic adds per 64-query x
+ *                      128-key step bound it by the chip's float32 atomic
+ *                      rate (about 3.2e11 adds/s on MI355X): at B=4 H=16
+ *                      N=4096 d=64 causal that is 2.8e8 adds, >= 0.86 ms,
+ *                      where the deterministic mode takes about 0.52 ms.
+ * Both modes meet the same tolerance against the exact gradients.
+ *
+ * Only FA_BF16 is accepted (FA_ERR_DTYPE otherwise).  Calls that share a
+ * workspace must not overlap.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dO, void* dq, void* dk, void* dv,
            int B, int H, int Nq, int Nk, int d, float scale, int causal,
-           int dtype, void* workspace, size_t workspace_bytes, void* stream);
+           int dtype, int deterministic, void* workspace, size_t workspace_bytes,
+           void* stream);
 
 /*
  * fa_bwd for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
- * arguments and results as fa_bwd (bitwise the same outputs), without the
- * workspace: its two row vectors live in a static device array of
+ * arguments and results as fa_bwd with deterministic = 1 (bitwise the same
+ * outputs), without the workspace: its two row vectors live in a static
+ * device array of
  * FA_NOALLOC_SCRATCH_BYTES held by each GPU the library runs on until the
  * process ends.  The call allocates and frees nothing.
  *
- * Limit: fa_bwd_workspace_bytes() of the call must not exceed
+ * Limit: fa_bwd_workspace_bytes(..., 1) of the call must not exceed
  * FA_NOALLOC_SCRATCH_BYTES, i.e. B * H * Nq <= 1,048,576 query rows (e.g.
  * B=8 H=32 N=4096, or B=1 H=32 N=32768); beyond it the call returns
  * FA_ERR_SCRATCH and enqueues nothing.  The first call on a device looks up
@@ -195,8 +218,8 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  * are skipped, so the work scales with the visible pairs.  A row with no
  * visible key gets O = 0 and LSE = -inf, as under the causal mask.
  *
- * Arguments, layouts, ownership, dtypes, determinism and errors are those
- * of fa_fwd and fa_bwd, with (window_left, window_right) in place of causal.
+ * Arguments, layouts, ownership, dtypes, modes and errors are those of
+ * fa_fwd and fa_bwd, with (window_left, window_right) in place of causal.
  * fa_bwd_window must be given the window its forward pass used.
  */
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -206,7 +229,7 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
 int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
                   int B, int H, int Nq, int Nk, int d, float scale,
-                  int window_left, int window_right, int dtype,
+                  int window_left, int window_right, int dtype, int deterministic,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -233,10 +256,11 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
  * cu_seqlens[B]) are not written.  Since the host never reads the offsets,
  * they may be produced on the stream just before the call.
  *
- * Only FA_BF16 (FA_ERR_DTYPE otherwise).  Deterministic.  B, H or total_q
- * equal to 0 is a no-op that returns FA_OK.  fa_bwd_varlen's workspace: at
- * least fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype) bytes (the two
- * row vectors of fa_bwd over the H * total_q packed rows); the same mask and
+ * Only FA_BF16 (FA_ERR_DTYPE otherwise).  The forward is deterministic;
+ * fa_bwd_varlen has fa_bwd's two modes.  B, H or total_q equal to 0 is a
+ * no-op that returns FA_OK.  fa_bwd_varlen's workspace: at least
+ * fa_bwd_varlen_workspace_bytes(H, total_q, d, dtype, deterministic) bytes
+ * (fa_bwd's workspace over the H * total_q packed rows); the same mask and
  * offsets as the forward call must be given.
  */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -244,14 +268,14 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
                   float scale, int window_left, int window_right, int dtype, void* stream);
 
-size_t fa_bwd_varlen_workspace_bytes(int H, int total_q, int d, int dtype);
+size_t fa_bwd_varlen_workspace_bytes(int H, int total_q, int d, int dtype, int deterministic);
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
                   const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
                   int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
                   float scale, int window_left, int window_right, int dtype,
-                  void* workspace, size_t workspace_bytes, void* stream);
+                  int deterministic, void* workspace, size_t workspace_bytes, void* stream);
 
 /* A static, human-readable description of a status code. */
 const char* fa_strerror(int status);

@@ -84,38 +84,47 @@ def test_fwd_empty_is_a_noop():
 
 
 def test_workspace_bytes():
-    n = fa.fa_bwd_workspace_bytes(4, 16, 4096, 4096, 64, fa.FA_BF16)
     rows = 4 * 16 * 4096
+    n = fa.fa_bwd_workspace_bytes(4, 16, 4096, 4096, 64, fa.FA_BF16, 1)
     assert n == 2 * rows * 4                   # two float32 row vectors, already 256-aligned
     assert n % 256 == 0
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_BF16) == 2 * 256
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 96, fa.FA_BF16) == 0
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_F32) == 0
-    assert fa.fa_bwd_workspace_bytes(-1, 1, 3, 5, 64, fa.FA_BF16) == 0
-    assert fa.fa_bwd_workspace_bytes(1, 1, 0, 5, 64, fa.FA_BF16) == 0
+    # the atomic mode adds the float32 dQ buffer
+    assert fa.fa_bwd_workspace_bytes(4, 16, 4096, 4096, 64, fa.FA_BF16, 0) == n + rows * 64 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_BF16, 1) == 2 * 256
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_BF16, 0) == 2 * 256 + 768
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 128, fa.FA_BF16, 7) == 2 * 256
+    for det in (0, 1):
+        assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 96, fa.FA_BF16, det) == 0
+        assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_F32, det) == 0
+        assert fa.fa_bwd_workspace_bytes(-1, 1, 3, 5, 64, fa.FA_BF16, det) == 0
+        assert fa.fa_bwd_workspace_bytes(1, 1, 0, 5, 64, fa.FA_BF16, det) == 0
 
 
 def bwd(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dO=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
              B=1, H=2, Nq=32, Nk=32, d=64, scale=0.125, causal=1, dtype=fa.FA_BF16,
-             workspace=FAKE, workspace_bytes=1 << 20, stream=0)
+             deterministic=0, workspace=FAKE, workspace_bytes=1 << 20, stream=0)
     a.update(kw)
     return fa.fa_bwd(**a)
 
 
 def test_bwd_validation_codes():
-    assert bwd(dtype=fa.FA_F32) == -4
-    assert bwd(d=32) == -3
-    assert bwd(Nk=-1) == -2
-    assert bwd(scale=0.0) == -8
-    assert bwd(dO=0) == -1
-    assert bwd(dk=0) == -1
-    assert bwd(lse=0) == -1
-    assert bwd(dq=FAKE_MIS) == -5
-    assert bwd(workspace=0) == -6
-    need = fa.fa_bwd_workspace_bytes(1, 2, 32, 32, 64, fa.FA_BF16)
-    assert bwd(workspace_bytes=need - 1) == -6
-    assert bwd(B=0) == 0
+    for det in (0, 1):
+        assert bwd(deterministic=det, dtype=fa.FA_F32) == -4
+        assert bwd(deterministic=det, d=32) == -3
+        assert bwd(deterministic=det, Nk=-1) == -2
+        assert bwd(deterministic=det, scale=0.0) == -8
+        assert bwd(deterministic=det, dO=0) == -1
+        assert bwd(deterministic=det, dk=0) == -1
+        assert bwd(deterministic=det, lse=0) == -1
+        assert bwd(deterministic=det, dq=FAKE_MIS) == -5
+        assert bwd(deterministic=det, workspace=0) == -6
+        need = fa.fa_bwd_workspace_bytes(1, 2, 32, 32, 64, fa.FA_BF16, det)
+        assert bwd(deterministic=det, workspace_bytes=need - 1) == -6
+        assert bwd(deterministic=det, B=0) == 0
+    # the atomic mode's workspace does not fit a deterministic-sized buffer
+    small = fa.fa_bwd_workspace_bytes(1, 2, 32, 32, 64, fa.FA_BF16, 1)
+    assert bwd(deterministic=0, workspace_bytes=small) == -6
 
 
 def bwd_noalloc(**kw):
@@ -134,7 +143,7 @@ def test_bwd_noalloc_validation_codes():
     assert bwd_noalloc(B=0, q=0, k=0, v=0, o=0, lse=0, dO=0, dq=0, dk=0, dv=0) == 0
     # the static array holds two fp32 vectors of up to 2^20 query rows
     limit = (8 << 20) // 8
-    assert fa.fa_bwd_workspace_bytes(8, 32, 4096, 4096, 128, fa.FA_BF16) == 8 << 20
+    assert fa.fa_bwd_workspace_bytes(8, 32, 4096, 4096, 128, fa.FA_BF16, 1) == 8 << 20
     assert 8 * 32 * 4096 == limit
     assert bwd_noalloc(B=1, H=1, Nq=limit + 1, Nk=64) == -10
     assert bwd_noalloc(B=3, H=32, Nq=limit // 96 + 64, Nk=64) == -10
@@ -198,7 +207,7 @@ def fwdw(**kw):
 def bwdw(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dO=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
              B=1, H=2, Nq=32, Nk=32, d=64, scale=0.125, window_left=8, window_right=4,
-             dtype=fa.FA_BF16, workspace=FAKE, workspace_bytes=1 << 20, stream=0)
+             dtype=fa.FA_BF16, deterministic=0, workspace=FAKE, workspace_bytes=1 << 20, stream=0)
     a.update(kw)
     return fa.fa_bwd_window(**a)
 
@@ -234,7 +243,8 @@ def bwdv(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dO=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
              cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, B=3, H=2, total_q=100, total_k=120,
              max_seqlen_q=50, max_seqlen_k=60, d=128, scale=0.125, window_left=-1,
-             window_right=-1, dtype=fa.FA_BF16, workspace=FAKE, workspace_bytes=1 << 20, stream=0)
+             window_right=-1, dtype=fa.FA_BF16, deterministic=1, workspace=FAKE,
+             workspace_bytes=1 << 20, stream=0)
     a.update(kw)
     return fa.fa_bwd_varlen(**a)
 
@@ -263,17 +273,24 @@ def test_varlen_validation_codes():
     assert bwdv(lse=0) == -1
     assert bwdv(dk=FAKE_MIS) == -5
     assert bwdv(workspace=0) == -6
-    need = fa.fa_bwd_varlen_workspace_bytes(2, 100, 128, fa.FA_BF16)
+    need = fa.fa_bwd_varlen_workspace_bytes(2, 100, 128, fa.FA_BF16, 1)
     assert need == 2 * 1024                 # 2 heads x 100 rows x 4 B -> 800 -> 1024, twice
     assert bwdv(workspace_bytes=need - 1) == -6
+    atomic = fa.fa_bwd_varlen_workspace_bytes(2, 100, 128, fa.FA_BF16, 0)
+    assert atomic == need + 200 * 128 * 4
+    assert bwdv(deterministic=0, workspace_bytes=atomic - 1) == -6
     assert bwdv(total_q=0, total_k=0, q=0, k=0) == 0
 
 
 def test_varlen_workspace_bytes():
-    assert fa.fa_bwd_varlen_workspace_bytes(16, 4096 * 4, 64, fa.FA_BF16) == 2 * 16 * 4096 * 4 * 4
-    assert fa.fa_bwd_varlen_workspace_bytes(1, 3, 64, fa.FA_BF16) == 512
-    assert fa.fa_bwd_varlen_workspace_bytes(1, 3, 64, fa.FA_F32) == 0
-    assert fa.fa_bwd_varlen_workspace_bytes(1, 3, 80, fa.FA_BF16) == 0
-    assert fa.fa_bwd_varlen_workspace_bytes(-1, 3, 64, fa.FA_BF16) == 0
+    ws = fa.fa_bwd_varlen_workspace_bytes
+    assert ws(16, 4096 * 4, 64, fa.FA_BF16, 1) == 2 * 16 * 4096 * 4 * 4
+    assert ws(16, 4096 * 4, 64, fa.FA_BF16, 0) == 2 * 16 * 4096 * 4 * 4 + 16 * 4096 * 4 * 64 * 4
+    assert ws(1, 3, 64, fa.FA_BF16, 1) == 512
+    assert ws(1, 3, 64, fa.FA_BF16, 0) == 512 + 768
+    for det in (0, 1):
+        assert ws(1, 3, 64, fa.FA_F32, det) == 0
+        assert ws(1, 3, 80, fa.FA_BF16, det) == 0
+        assert ws(-1, 3, 64, fa.FA_BF16, det) == 0
     # more rows per head than FA_MAX_SEQ are fine when packed
-    assert fa.fa_bwd_varlen_workspace_bytes(2, 1 << 24, 64, fa.FA_BF16) == 2 * 2 * (1 << 24) * 4
+    assert ws(2, 1 << 24, 64, fa.FA_BF16, 1) == 2 * 2 * (1 << 24) * 4

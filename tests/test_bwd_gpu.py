@@ -1,4 +1,7 @@
-"""GPU parity of fa_bwd (recomputation backward) against the fp64 oracle.
+"""GPU parity of fa_bwd (recomputation backward) against the fp64 oracle, in
+both modes: the deterministic one (dQ from its own kernel, bitwise
+repeatable) and the atomic one (one key-side kernel, dQ summed with fp32
+atomics).
 
 The GPU backward consumes the GPU forward's O and LSE, as a training step
 does; the oracle computes everything from the same bf16 inputs in fp64.
@@ -20,12 +23,17 @@ def banner(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def gpu_fwd_bwd(q, k, v, do, scale, causal):
+def gpu_fwd_bwd(q, k, v, do, scale, causal, deterministic):
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     o, lse = fa.attention_forward(qd, kd, vd, scale=scale, causal=causal)
-    dq, dk, dv = fa.attention_backward(qd, kd, vd, o, lse, dod, scale=scale, causal=causal)
+    dq, dk, dv = fa.attention_backward(qd, kd, vd, o, lse, dod, scale=scale, causal=causal,
+                                       deterministic=deterministic)
     torch.cuda.synchronize()
     return dq, dk, dv
+
+
+MODES = [False, True]
+mode_id = lambda det: "det" if det else "atomic"
 
 
 SMALL = [
@@ -41,13 +49,14 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("det", MODES, ids=mode_id)
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
-def test_backward_small_and_ragged(case):
+def test_backward_small_and_ragged(case, det):
     B, H, Nq, Nk, d, causal = case
-    banner(f"bwd small {case}")
+    banner(f"bwd small {case} {mode_id(det)}")
     q, k, v, do = wl.make_inputs(B, H, Nq, Nk, d, "bf16", seed=500 + Nq + Nk + d, with_do=True)
     scale = 1.0 / np.sqrt(d)
-    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, scale, causal)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, scale, causal, det)
     rq, rk, rv, *_ = attention_backward(to64(q), to64(k), to64(v), to64(do), scale, causal)
     check_grad(to64(dq), rq, f"dq {case}")
     check_grad(to64(dk), rk, f"dk {case}")
@@ -65,14 +74,15 @@ PAIRED = [
 ]
 
 
+@pytest.mark.parametrize("det", MODES, ids=mode_id)
 @pytest.mark.parametrize("case", PAIRED, ids=lambda c: "-".join(map(str, c)))
-def test_backward_paired_tiles_sampled_heads(case):
+def test_backward_paired_tiles_sampled_heads(case, det):
     B, H, Nq, Nk, d = case
     assert B * H * ((min(Nq, Nk) + 127) // 128) >= 2048   # both kernels pair
-    banner(f"bwd paired {case}")
+    banner(f"bwd paired {case} {mode_id(det)}")
     q, k, v, do = wl.make_inputs(B, H, Nq, Nk, d, "bf16", seed=700 + Nq + Nk + d, with_do=True)
     scale = 1.0 / np.sqrt(d)
-    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, scale, True)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, scale, True, det)
     for bh in (0, B * H // 2, B * H - 1):
         b, h = divmod(bh, H)
         rq, rk, rv, *_ = attention_backward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]),
@@ -89,11 +99,12 @@ def sampled_heads(w, seed, n=16):
     return [0, w.B * w.H - 1] + others[: n - 2]
 
 
-def test_train_step_workload_sampled_heads():
+@pytest.mark.parametrize("det", MODES, ids=mode_id)
+def test_train_step_workload_sampled_heads(det):
     w = wl.TRAIN_STEP
-    banner(w.describe())
+    banner(w.describe() + " " + mode_id(det))
     q, k, v, do = wl.workload_inputs(w)
-    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, w.scale, w.causal)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, w.scale, w.causal, det)
     heads = sampled_heads(w, 5050)
     for bh in heads:
         b, h = divmod(bh, w.H)
@@ -105,14 +116,15 @@ def test_train_step_workload_sampled_heads():
         check_grad(to64(dv[b, h]), rv, f"dv head {bh}")
 
 
-def test_llama_causal_backward_sampled_heads():
-    """The d = 128 backward at B=4 H=32 N=4096 causal (dQ, dV and dK each from
-    their own kernel), on the inputs bench.py times with --train-workload
-    llama_causal_bf16 (the workload's seed, dO drawn after Q, K, V)."""
+@pytest.mark.parametrize("det", MODES, ids=mode_id)
+def test_llama_causal_backward_sampled_heads(det):
+    """The d = 128 backward at B=4 H=32 N=4096 causal, on the inputs bench.py
+    times with --train-workload llama_causal_bf16 (the workload's seed, dO
+    drawn after Q, K, V)."""
     w = wl.LLAMA_CAUSAL
-    banner(w.describe() + " (backward)")
+    banner(w.describe() + " (backward) " + mode_id(det))
     q, k, v, do = wl.make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, with_do=True)
-    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, w.scale, w.causal)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, w.scale, w.causal, det)
     heads = sampled_heads(w, 5151)
     for bh in heads:
         b, h = divmod(bh, w.H)
@@ -124,13 +136,23 @@ def test_llama_causal_backward_sampled_heads():
         check_grad(to64(dv[b, h]), rv, f"dv head {bh}")
 
 
-def test_backward_invariants_and_repeatability():
-    banner("bwd invariants")
-    q, k, v, do = wl.make_inputs(1, 2, 256, 256, 64, "bf16", seed=61, with_do=True)
-    dq1, dk1, dv1 = gpu_fwd_bwd(q, k, v, do, 0.125, True)
-    dq2, dk2, dv2 = gpu_fwd_bwd(q, k, v, do, 0.125, True)
-    # every gradient is accumulated by one workgroup: bitwise repeatable
-    assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("det", MODES, ids=mode_id)
+def test_backward_invariants_and_repeatability(det, d):
+    banner(f"bwd invariants d={d} {mode_id(det)}")
+    q, k, v, do = wl.make_inputs(1, 2, 256, 256, d, "bf16", seed=61, with_do=True)
+    dq1, dk1, dv1 = gpu_fwd_bwd(q, k, v, do, 0.125, True, det)
+    runs = [gpu_fwd_bwd(q, k, v, do, 0.125, True, det) for _ in range(3)]
+    for dq2, dk2, dv2 in runs:
+        # dK and dV are accumulated by one workgroup in both modes; dQ too in
+        # the deterministic mode, while the atomic mode's fp32 adds may land
+        # in any order (same tolerance, not bitwise)
+        assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+        if det:
+            assert torch.equal(dq1, dq2)
+        else:
+            err = (dq1.float() - dq2.float()).abs().max().item()
+            assert err <= 2e-2 * max(1.0, dq1.float().abs().max().item())
     # rows of dS sum to zero, so the key gradients sum to ~0; sum_j dV_j = sum_i dO_i
     ksum = dk1.float().sum(dim=2).abs().max().item()
     kscale = dk1.float().abs().sum(dim=2).max().item()
@@ -147,13 +169,18 @@ def test_binding_checks_devices_and_sizes_workspace_in_bytes():
     with pytest.raises(ValueError):
         fa.attention_forward(qd, k, vd, causal=True)          # k left on the host
     o, lse = fa.attention_forward(qd, kd, vd, causal=True)
-    need = fa.fa_bwd_workspace_bytes(1, 2, 100, 100, 64, fa.FA_BF16)
+    need = fa.fa_bwd_workspace_bytes(1, 2, 100, 100, 64, fa.FA_BF16, 1)
     with pytest.raises(ValueError):
         fa.attention_backward(qd, kd, vd, o, lse, dod, causal=True,
-                              workspace=torch.empty(need, dtype=torch.uint8))
+                              workspace=torch.empty(need, dtype=torch.uint8), deterministic=True)
     # a float32 workspace: at least `need` bytes in fewer than `need` elements
     ws = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
-    dq, dk, dv = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=True, workspace=ws)
-    dq0, dk0, dv0 = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=True)
+    dq, dk, dv = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=True, workspace=ws,
+                                       deterministic=True)
+    dq0, dk0, dv0 = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=True, deterministic=True)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq0) and torch.equal(dk, dk0) and torch.equal(dv, dv0)
+    # the atomic mode refuses the smaller, deterministic-sized workspace
+    with pytest.raises(fa.FAError):
+        fa.attention_backward(qd, kd, vd, o, lse, dod, causal=True, workspace=ws,
+                              deterministic=False)

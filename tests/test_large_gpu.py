@@ -25,7 +25,8 @@ def banner(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def test_forward_and_backward_past_2_31_elements():
+@pytest.mark.parametrize("det", [False, True], ids=lambda x: "det" if x else "atomic")
+def test_forward_and_backward_past_2_31_elements(det):
     B, H, N, d = 40, 128, 4096, 128
     per_head = N * d
     assert B * H * per_head > 2 ** 31
@@ -33,7 +34,8 @@ def test_forward_and_backward_past_2_31_elements():
     banner(f"large fwd+bwd B{B} H{H} N{N} d{d} causal ({B * H * per_head} elements per tensor)")
     q, k, v, do = wl.make_inputs_device(B, H, N, N, d, "bf16", seed=7007, device="cuda", with_do=True)
     o, lse = fa.attention_forward(q, k, v, scale=scale, causal=True)
-    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, scale=scale, causal=True)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, scale=scale, causal=True,
+                                       deterministic=det)
     torch.cuda.synchronize()
     first_past = 2 ** 31 // per_head            # first head starting at element 2^31 (byte 2^32)
     heads = [0, first_past // 2 - 1, first_past // 2, first_past - 1, first_past, B * H - 1]

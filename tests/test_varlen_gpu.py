@@ -40,14 +40,16 @@ def run_fwd(q, k, v, cu_q, cu_k, lens_q, lens_k, scale, causal=False, window=Non
     return o, l
 
 
-def run_fwd_bwd(q, k, v, do, cu_q, cu_k, lens_q, lens_k, scale, causal=False, window=None):
+def run_fwd_bwd(q, k, v, do, cu_q, cu_k, lens_q, lens_k, scale, causal=False, window=None,
+                deterministic=False):
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     cq, ck = cu_q.cuda(), cu_k.cuda()
     mq, mk = max(lens_q, default=0), max(lens_k, default=0)
     o, lse = fa.attention_forward_varlen(qd, kd, vd, cq, ck, mq, mk, scale=scale, causal=causal,
                                          window=window)
     dq, dk, dv = fa.attention_backward_varlen(qd, kd, vd, o, lse, dod, cq, ck, mq, mk, scale=scale,
-                                              causal=causal, window=window)
+                                              causal=causal, window=window,
+                                              deterministic=deterministic)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
@@ -94,15 +96,17 @@ BWD = [
 ]
 
 
+@pytest.mark.parametrize("det", [False, True], ids=lambda x: "det" if x else "atomic")
 @pytest.mark.parametrize("case", BWD, ids=lambda c: "-".join(map(str, c)).replace(" ", ""))
-def test_varlen_backward_small_and_ragged(case):
+def test_varlen_backward_small_and_ragged(case, det):
     lens_q, lens_k, d, causal, window = case
     lens_k = lens_q if lens_k is None else lens_k
-    banner(f"varlen bwd {case}")
+    banner(f"varlen bwd {case} {'det' if det else 'atomic'}")
     q, k, v, do, cu_q, cu_k = wl.make_varlen_inputs(lens_q, lens_k, 2, d, "bf16",
                                                     seed=3300 + sum(lens_k) + d, with_do=True)
     scale = 1.0 / np.sqrt(d)
-    _, _, dq, dk, dv = run_fwd_bwd(q, k, v, do, cu_q, cu_k, lens_q, lens_k, scale, causal, window)
+    _, _, dq, dk, dv = run_fwd_bwd(q, k, v, do, cu_q, cu_k, lens_q, lens_k, scale, causal, window,
+                                   deterministic=det)
     rq, rk, rv = varlen_backward(to64(q), to64(k), to64(v), to64(do), cu_q.numpy(), cu_k.numpy(),
                                  scale, causal, window)
     check_grad(to64(dq), rq, f"dq {case}")
@@ -117,11 +121,11 @@ def test_varlen_equal_lengths_reproduce_fixed_length_bitwise(d, causal):
     q, k, v, do = wl.make_inputs(B, H, N, N, d, "bf16", seed=3600 + d, with_do=True)
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     o, lse = fa.attention_forward(qd, kd, vd, causal=causal)
-    dq, dk, dv = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=causal)
+    dq, dk, dv = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=causal, deterministic=True)
     pack = lambda x: x.transpose(0, 1).reshape(H, B * N, d).contiguous()   # [B,H,N,d] -> [H,B*N,d]
     cu = torch.arange(B + 1, dtype=torch.int32) * N
     got = run_fwd_bwd(pack(q), pack(k), pack(v), pack(do), cu, cu, [N] * B, [N] * B,
-                      1.0 / np.sqrt(d), causal)
+                      1.0 / np.sqrt(d), causal, deterministic=True)
     ref = (pack(o), lse.transpose(0, 1).reshape(H, B * N), pack(dq), pack(dk), pack(dv))
     for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), ref, got):
         assert torch.equal(a, b), name
@@ -131,8 +135,8 @@ def test_varlen_is_deterministic():
     banner("varlen determinism")
     lens = [300, 77, 512, 129]
     q, k, v, do, cu, _ = wl.make_varlen_inputs(lens, lens, 2, 64, "bf16", seed=3700, with_do=True)
-    a = run_fwd_bwd(q, k, v, do, cu, cu, lens, lens, 0.125, True)
-    b = run_fwd_bwd(q, k, v, do, cu, cu, lens, lens, 0.125, True)
+    a = run_fwd_bwd(q, k, v, do, cu, cu, lens, lens, 0.125, True, deterministic=True)
+    b = run_fwd_bwd(q, k, v, do, cu, cu, lens, lens, 0.125, True, deterministic=True)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 

@@ -36,11 +36,11 @@ def gpu_fwd(q, k, v, scale, window=None, causal=False):
     return o, lse
 
 
-def gpu_fwd_bwd(q, k, v, do, scale, window=None, causal=False):
+def gpu_fwd_bwd(q, k, v, do, scale, window=None, causal=False, deterministic=False):
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     o, lse = fa.attention_forward(qd, kd, vd, scale=scale, causal=causal, window=window)
     dq, dk, dv = fa.attention_backward(qd, kd, vd, o, lse, dod, scale=scale, causal=causal,
-                                       window=window)
+                                       window=window, deterministic=deterministic)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
@@ -85,13 +85,14 @@ BWD = [
 ]
 
 
+@pytest.mark.parametrize("det", [False, True], ids=lambda x: "det" if x else "atomic")
 @pytest.mark.parametrize("case", BWD, ids=lambda c: "-".join(map(str, c)))
-def test_window_backward_small_and_ragged(case):
+def test_window_backward_small_and_ragged(case, det):
     B, H, Nq, Nk, d, window = case
-    banner(f"window bwd {case}")
+    banner(f"window bwd {case} {'det' if det else 'atomic'}")
     q, k, v, do = wl.make_inputs(B, H, Nq, Nk, d, "bf16", seed=1500 + Nq + Nk + d, with_do=True)
     scale = 1.0 / np.sqrt(d)
-    _, _, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, scale, window)
+    _, _, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, scale, window, deterministic=det)
     rq, rk, rv, *_ = attention_backward(to64(q), to64(k), to64(v), to64(do), scale, False,
                                         window=window)
     check_grad(to64(dq), rq, f"dq {case}")
@@ -104,15 +105,16 @@ def test_window_limits_reproduce_causal_and_unmasked_bitwise(d):
     banner(f"window limits d={d}")
     q, k, v, do = wl.make_inputs(1, 2, 390, 450, d, "bf16", seed=1700 + d, with_do=True)
     scale = 1.0 / np.sqrt(d)
-    c = gpu_fwd_bwd(q, k, v, do, scale, causal=True)
-    n = gpu_fwd_bwd(q, k, v, do, scale, causal=False)
+    # bitwise comparisons: the deterministic backward
+    c = gpu_fwd_bwd(q, k, v, do, scale, causal=True, deterministic=True)
+    n = gpu_fwd_bwd(q, k, v, do, scale, causal=False, deterministic=True)
     # the causal and unmasked kernels through the window entry points
-    wc = gpu_fwd_bwd(q, k, v, do, scale, window=(None, 0))
-    wn = gpu_fwd_bwd(q, k, v, do, scale, window=(None, None))
+    wc = gpu_fwd_bwd(q, k, v, do, scale, window=(None, 0), deterministic=True)
+    wn = gpu_fwd_bwd(q, k, v, do, scale, window=(None, None), deterministic=True)
     # the window kernels with bounds that hide nothing beyond the causal
     # diagonal (left reach past every key), and nothing at all
-    bc = gpu_fwd_bwd(q, k, v, do, scale, window=(10**6, 0))
-    bn = gpu_fwd_bwd(q, k, v, do, scale, window=(10**6, 10**6))
+    bc = gpu_fwd_bwd(q, k, v, do, scale, window=(10**6, 0), deterministic=True)
+    bn = gpu_fwd_bwd(q, k, v, do, scale, window=(10**6, 10**6), deterministic=True)
     names = ("o", "lse", "dq", "dk", "dv")
     for ref, got, what in ((c, wc, "(None,0)"), (n, wn, "(None,None)"),
                            (c, bc, "(1e6,0)"), (n, bn, "(1e6,1e6)")):

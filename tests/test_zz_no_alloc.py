@@ -1,5 +1,6 @@
 """fa_bwd_noalloc (the backward with its workspace in a static device array)
-against fa_bwd with a caller workspace, through the C ABI.
+against fa_bwd in its deterministic mode with a caller workspace, through the
+C ABI.
 
 Both run the same kernels on the same inputs, so the gradients must agree
 bitwise; the first call is also checked against the fp64 oracle.  Calls run
@@ -61,7 +62,7 @@ def test_noalloc_matches_fa_bwd_on_calls_in_a_row():
     for i, (B, H, Nq, Nk, d, causal) in enumerate(CALLS):
         banner(f"noalloc call {i}: {(B, H, Nq, Nk, d, causal)}")
         q, k, v, o, lse, do, scale = inputs(B, H, Nq, Nk, d, causal, seed=6100 + i)
-        ref = fa.attention_backward(q, k, v, o, lse, do, scale=scale, causal=causal)
+        ref = fa.attention_backward(q, k, v, o, lse, do, scale=scale, causal=causal, deterministic=True)
         torch.cuda.synchronize()
         got, used = noalloc(q, k, v, o, lse, do, scale, causal)
         if i > 0:
