@@ -296,6 +296,42 @@ def atomic_probe(grid: int = 8192, repeats: int = 5) -> dict:
             "adds_per_s": round(n / (ms * 1e-3), -8), "ms": round(ms, 4), "adds": n}
 
 
+def valu_probe(sclk_ghz: float, repeats: int = 5) -> dict:
+    """Cycles a wave's v_exp_f32 and v_fma_f32 hold a SIMD (libfa_probe.so,
+    8 waves per SIMD, 8 independent chains per lane), at the core clock
+    ``sclk_ghz``: an exponential (with its add), two FMAs, and both mixed --
+    mixed near the sum of the two means the exponential shares the FMA pipe."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_20_amd", "libfa_probe.so"))
+    lib.fa_probe_valu_launch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_long), ctypes.POINTER(ctypes.c_long)]
+    grid = 256 * 32
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for variant, name in ((0, "exp+add"), (1, "fma x2"), (2, "exp+add, fma x2")):
+        ne, no = ctypes.c_long(), ctypes.c_long()
+        ts = []
+        for _ in range(repeats + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = lib.fa_probe_valu_launch(ctypes.c_void_p(out.data_ptr()), grid, variant,
+                                          ctypes.c_void_p(stream.cuda_stream), ctypes.byref(ne), ctypes.byref(no))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if st != 0:
+                raise RuntimeError(f"fa_probe_valu_launch failed with {st}")
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts[1:])[repeats // 2]
+        waves_per_simd = grid * 4 / 1024
+        cyc_per_step = ms * 1e-3 * sclk_ghz * 1e9 / waves_per_simd / (ne.value or no.value // (2 if variant == 1 else 3))
+        res[name] = {"ms": round(ms, 4), "cycles_per_step": round(cyc_per_step, 2)}
+    res["note"] = ("cycles one wave's step holds its SIMD (8 waves per SIMD); a step is one chain's "
+                   "exp+add, two FMAs, or both")
+    return res
+
+
 def time_launches(fn, stream, steps: int, warmup: int) -> float:
     """Average ms per call of ``fn`` with HIP events on ``stream``."""
     import torch
@@ -504,6 +540,44 @@ def _counter_means(csv_dir: str, counter: str):
     return {k: v[0] / v[1] for k, v in sums.items()}
 
 
+def summarize_sq(csv_dirs, sclk_ghz: float) -> str:
+    """Markdown table of per-dispatch means of every counter in the
+    rocprofv3 --pmc CSVs of ``csv_dirs``, one row per kernel variant (name,
+    grid, VGPRs, LDS bytes), with the dispatch duration and, where the SQ
+    counters are there, other VALU instructions and LDS instructions per MFMA
+    and the MFMA pipes' busy share: SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs
+    x duration x ``sclk_ghz``."""
+    import csv
+    import glob
+    rows = {}
+    for d in csv_dirs:
+        for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    key = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["VGPR_Count"]) + int(r["Accum_VGPR_Count"]),
+                           int(r["LDS_Block_Size"]))
+                    disp = rows.setdefault(key, {})
+                    c = disp.setdefault((path, r["Dispatch_Id"]), {})
+                    c[r["Counter_Name"]] = float(r["Counter_Value"])
+                    c["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    names = sorted({n for disp in rows.values() for c in disp.values() for n in c if not n.startswith("_")})
+    out = ["| kernel (grid, VGPRs, LDS B) | dispatches | us | " + " | ".join(names) +
+           " | other VALU / MFMA | LDS / MFMA | MFMA busy |",
+           "|---" * (len(names) + 6) + "|"]
+    for key, disp in sorted(rows.items(), key=lambda kv: -len(kv[1])):
+        n = len(disp)
+        mean = {nm: sum(c.get(nm, 0.0) for c in disp.values()) / n for nm in names}
+        us = sum(c["_ns"] for c in disp.values()) / n / 1e3
+        mf = mean.get("SQ_INSTS_MFMA", 0.0)
+        valu = f"{(mean['SQ_INSTS_VALU'] - mf) / mf:.2f}" if mf and "SQ_INSTS_VALU" in mean else ""
+        lds = f"{mean['SQ_INSTS_LDS'] / mf:.2f}" if mf and "SQ_INSTS_LDS" in mean else ""
+        busy = (f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * us * 1e3 * sclk_ghz):.3f}"
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in mean else "")
+        out.append(f"| {key[0]} ({key[1] // 256 if key[1] % 256 == 0 else key[1]}, {key[2]}, {key[3]}) | {n} | "
+                   f"{us:.1f} | " + " | ".join(f"{mean[nm]:,.0f}" for nm in names) + f" | {valu} | {lds} | {busy} |")
+    return "\n".join(out)
+
+
 def summarize_counters(workload: str, kernel: str, fetch_dir: str, write_dir: str,
                        copy_fetch_dir: str, copy_write_dir: str, copy_mib: int) -> dict:
     """HBM bytes per launch of ``kernel`` from two --pmc runs (FETCH_SIZE,
@@ -559,7 +633,27 @@ def main():
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "COPY_MIB"),
                     help="write profiles/traffic.json for --workload from rocprofv3 --pmc output "
                          "directories (no GPU needed)")
+    ap.add_argument("--probes", action="store_true",
+                    help="print the MFMA, float32 atomic and VALU (exp vs FMA) probes of "
+                         "libfa_probe.so as one JSON line and exit")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="PMC_DIR",
+                    help="print per-kernel means of the counters in rocprofv3 --pmc output "
+                         "directories as a markdown table (no GPU needed)")
+    ap.add_argument("--sclk-ghz", type=float, default=2.1,
+                    help="core clock for --summarize-sq's MFMA busy share")
     args = ap.parse_args()
+    if args.probes:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py --probes needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        mp = mfma_probe()
+        print(json.dumps({"mfma": mp, "atomic": atomic_probe(), "valu": valu_probe(mp["sclk_ghz"]),
+                          "device": device_description()}), flush=True)
+        return
+    if args.summarize_sq:
+        print(summarize_sq(args.summarize_sq, args.sclk_ghz))
+        return
     if args.summarize_counters:
         fd, wd, cfd, cwd, mib = args.summarize_counters
         kern = "fwd_bf16_kernel" if "bf16" in args.workload else "fwd_f32_kernel"

@@ -580,8 +580,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 //
 // Cost: one float32 atomic add per (query row, head-dim column, 128-key
 // tile), 64 x d per step, and MI355X retires about 3.2e11 such adds per
-// second chip-wide (buffer atomics to distinct addresses, measured), a
-// quarter of its plain-store rate.  That bounds this kernel well above the
+// second chip-wide (buffer atomics to distinct addresses, measured, 1.3 TB/s
+// of payload).  That bounds this kernel well above the
 // two deterministic kernels' time (0.87 vs 0.52 ms at B=4 H=16 N=4096 d=64
 // causal), which is why the deterministic mode is the default.
 // ---------------------------------------------------------------------------

@@ -3,7 +3,9 @@
 //     load, and the core clock while they do -- bench.py reports it beside
 //     the published 2.5 PFLOP/s peak as a measured denominator;
 //   * the chip-wide rate of float32 buffer atomic adds to distinct
-//     addresses -- the bound of the backward's atomic-dQ mode.
+//     addresses -- the bound of the backward's atomic-dQ mode;
+//   * the VALU cost of v_exp_f32 against v_fma_f32 (is the exponential a
+//     separate pipe, and what would a polynomial 2^x on the FMA path cost).
 //
 // Each wave runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 on four
 // independent accumulator chains (no memory traffic inside the loop), so the
@@ -82,5 +84,47 @@ extern "C" int fa_probe_atomic_launch(void* buf, int grid, void* stream) {
     if (!buf || grid <= 0 || fa_probe_atomic_elems(grid) * 4 > 0xffffffffL) return -1;
     hipLaunchKernelGGL(probe_atomic_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (float*)buf,
                        (uint32_t)fa_probe_atomic_elems(grid));
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+// VALU issue costs: each lane runs 8 independent chains for kValuIters
+// steps; a step is NE x (v_exp_f32 then one add) and NF x v_fma_f32 per
+// chain.  With 8 waves per SIMD (grid = 32 workgroups per CU) the time per
+// wave-step and SIMD gives the cycles each instruction holds the pipe.
+constexpr int kValuIters = 2048;
+
+template <int NE, int NF>
+__global__ void __launch_bounds__(256) probe_valu_kernel(float* out, float a) {
+    float x[8], y[8];
+    for (int i = 0; i < 8; ++i) {
+        x[i] = -0.001f * (float)(threadIdx.x + i);
+        y[i] = 0.5f + 0.01f * (float)i;
+    }
+    for (int it = 0; it < kValuIters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int e = 0; e < NE; ++e) x[i] = __builtin_amdgcn_exp2f(x[i]) - 1.0f;
+#pragma unroll
+            for (int f = 0; f < NF; ++f) y[i] = fmaf(y[i], a, 0.25f);
+        }
+    }
+    float sum = 0.f;
+    for (int i = 0; i < 8; ++i) sum += x[i] + y[i];
+    out[(size_t)blockIdx.x * 256 + threadIdx.x] = sum;
+}
+
+// variant 0: exp + add; 1: two FMAs; 2: exp + add and two FMAs.  out: grid *
+// 256 floats.  Returns the instruction counts of one wave through *n_exp,
+// *n_other (adds and FMAs), 0, or -1 / -7.
+extern "C" int fa_probe_valu_launch(void* out, int grid, int variant, void* stream, long* n_exp, long* n_other) {
+    if (!out || grid <= 0 || variant < 0 || variant > 2 || !n_exp || !n_other) return -1;
+    const long steps = (long)kValuIters * 8;
+    hipStream_t s = (hipStream_t)stream;
+    if (variant == 0) hipLaunchKernelGGL((probe_valu_kernel<1, 0>), dim3(grid), dim3(256), 0, s, (float*)out, 0.999f);
+    if (variant == 1) hipLaunchKernelGGL((probe_valu_kernel<0, 2>), dim3(grid), dim3(256), 0, s, (float*)out, 0.999f);
+    if (variant == 2) hipLaunchKernelGGL((probe_valu_kernel<1, 2>), dim3(grid), dim3(256), 0, s, (float*)out, 0.999f);
+    *n_exp = variant == 1 ? 0 : steps;
+    *n_other = variant == 0 ? steps : variant == 1 ? 2 * steps : 3 * steps;
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
