@@ -5,7 +5,8 @@
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Two launches on the caller's stream, no atomics (deterministic):
+// Deterministic mode (the default): two launches on the caller's stream, no
+// atomics:
 //   1. dQ   : one workgroup per (batch*head, 128-query tile) walking the key
 //             tiles it can see, like the forward pass.  Each wave owns 32
 //             queries: Q and dO sit in registers, K / V tiles stream through
@@ -16,10 +17,12 @@
 //   2. dK/dV: one workgroup per (batch*head, 128-key tile) walking the query
 //             tiles that can see it (the loop order of §5), reading D and
 //             LSE2 from the workspace.  Each wave owns 32 keys: K and V sit in
-//             registers, Q / dO tiles stream through LDS, dK and dV
-//             accumulate in registers for the whole walk.
+//             registers (d = 64; at d = 128 two waves share a 32-key slice,
+//             K and V sit in LDS, section 4), Q / dO tiles stream through
+//             LDS, dK and dV accumulate in registers for the whole walk.
 // S and dP are computed in both (7 products instead of 5) in exchange for no
-// dQ atomics and no dS round trip through memory.
+// dQ atomics and no dS round trip through memory.  The atomic mode (section
+// 4) computes all five in one key-side kernel.
 //
 // Register formulation (32x32x16 bf16 MFMA, fp32 accumulate).  In each main
 // kernel the products over the head dimension (S, dP) take the streamed tile
@@ -52,13 +55,12 @@ __device__ __forceinline__ void pack_pairs(const float (&x)[16], u32x4& lo, u32x
 // values of LSE*log2e and D; two stages, the next one filled while the
 // current one is used.
 // ---------------------------------------------------------------------------
-// PART: 0 computes dK and dV, 1 only dV (S and P^T dO), 2 only dK (S, dP,
-// dS and dS^T Q).  At d = 128 both accumulators, K and V do not fit two
-// waves per SIMD (about 440 registers), so the key side runs as a dV kernel
-// and a dK kernel, recomputing S in each, at two waves per SIMD.
-template <int D, int MASK, bool VARLEN = false, int PART = 0>
-__global__ void __launch_bounds__(256, (D == 64 || PART != 0) ? 2 : 1) bwd_dkdv_kernel(BwdParams p) {
-    constexpr bool kDV = PART != 2, kDK = PART != 1;
+// d = 64 only: at d = 128, K, V, dK and dV of a wave's 32 keys do not fit two
+// waves per SIMD, and the key side is bwd_fused_kernel without its dQ part
+// (eight waves, two per 32-key slice, each taking half of every step).
+template <int D, int MASK, bool VARLEN = false>
+__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
+    static_assert(D == 64, "the d = 128 key side is bwd_fused_kernel<128, ..., false>");
     constexpr int BKV = 128, BQ = 64;
     constexpr int NQB = BQ / 32;              // 32-query blocks per step
     constexpr int NQC = BQ / 16;              // 16-query k-steps
@@ -117,7 +119,7 @@ __global__ void __launch_bounds__(256, (D == 64 || PART != 0) ? 2 : 1) bwd_dkdv_
     for (int kk = 0; kk < NKK; ++kk) {
         const uint32_t o = (uint32_t)kj * D * 2 + (16 * kk + 8 * hg) * 2;
         kreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rk, o, 0));
-        if constexpr (kDK) vreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rv, o, 0));
+        vreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rv, o, 0));
     }
 
     // Query range: the walk starts at the first query tile that sees the
@@ -176,7 +178,7 @@ __global__ void __launch_bounds__(256, (D == 64 || PART != 0) ? 2 : 1) bwd_dkdv_
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         mark_loaded(kreg[kk]);
-        if constexpr (kDK) mark_loaded(vreg[kk]);
+        mark_loaded(vreg[kk]);
     }
 
     for (int qt = qt0; qt < n_qt; ++qt) {
@@ -205,23 +207,10 @@ __global__ void __launch_bounds__(256, (D == 64 || PART != 0) ? 2 : 1) bwd_dkdv_
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     s[qb] = mfma_bf16(tile_read_row<D>(qs, qb * 32, kk, lane), kreg[kk], s[qb]);
-                    if constexpr (kDK)
-                        dp[qb] = mfma_bf16(tile_read_row<D>(dos, qb * 32, kk, lane), vreg[kk], dp[qb]);
+                    dp[qb] = mfma_bf16(tile_read_row<D>(dos, qb * 32, kk, lane), vreg[kk], dp[qb]);
                 }
-            // At d = 128 the operand reads run four ahead of the MFMAs here and
-            // two per MFMA in the products below (+4.9% on the Llama-shaped
-            // backward); at d = 64 the compiler's own order measured 1.8% faster.
-            if constexpr (D == 128) {
-                constexpr int nm = (kDK ? 2 : 1) * NKK * NQB;
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-                for (int i = 0; i < nm - 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            }
+            // (the compiler's own order of the operand reads: an explicit
+            // four-ahead order measured 1.8% slower at d = 64)
             // ---- P = 2^(S*scale*log2e - LSE2), dS = P * (dP - D) ----
             // ---- mask: only steps that straddle a bound or the tail ----
             const bool need_mask = (q0 + BQ > Nq) || (kRight && q0 + offr < kw + 31) ||
@@ -250,38 +239,27 @@ __global__ void __launch_bounds__(256, (D == 64 || PART != 0) ? 2 : 1) bwd_dkdv_
                     const int ql = qb * 32 + g * 8 + 4 * hg;   // local query of item 4g
                     const f32x4 l2 = *(const f32x4*)(l2s + ql);
                     f32x4 dd = {};
-                    if constexpr (kDK) dd = *(const f32x4*)(dds + ql);
+                    dd = *(const f32x4*)(dds + ql);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float sv = s[qb][4 * g + e];
                         const float pe = exp2_hw(fmaf(sv, p.scale_log2, -l2[e]));
                         pv[4 * g + e] = pe;
-                        if constexpr (kDK) dsv[4 * g + e] = pe * (dp[qb][4 * g + e] - dd[e]);
+                        dsv[4 * g + e] = pe * (dp[qb][4 * g + e] - dd[e]);
                     }
                 }
-                if constexpr (kDV) pack_pairs(pv, pw[2 * qb], pw[2 * qb + 1]);
-                if constexpr (kDK) pack_pairs(dsv, dsw[2 * qb], dsw[2 * qb + 1]);
+                pack_pairs(pv, pw[2 * qb], pw[2 * qb + 1]);
+                pack_pairs(dsv, dsw[2 * qb], dsw[2 * qb + 1]);
             }
             // ---- dV^T += dO^T P ;  dK^T += Q^T dS ----
 #pragma unroll
             for (int qc = 0; qc < NQC; ++qc) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    if constexpr (kDV)
-                        dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qc * 16, db * 32, lane),
-                                              __builtin_bit_cast(bf16x8, pw[qc]), dvacc[db]);
-                    if constexpr (kDK)
-                        dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qc * 16, db * 32, lane),
-                                              __builtin_bit_cast(bf16x8, dsw[qc]), dkacc[db]);
-                }
-            }
-            if constexpr (D == 128) {   // two transposed reads per MFMA
-                constexpr int nm = ((kDV ? 1 : 0) + (kDK ? 1 : 0)) * NQC * NDB;
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-                for (int i = 0; i < nm; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                    if (i < nm - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+                    dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qc * 16, db * 32, lane),
+                                          __builtin_bit_cast(bf16x8, pw[qc]), dvacc[db]);
+                    dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qc * 16, db * 32, lane),
+                                          __builtin_bit_cast(bf16x8, dsw[qc]), dkacc[db]);
                 }
             }
         }
@@ -306,18 +284,13 @@ __global__ void __launch_bounds__(256, (D == 64 || PART != 0) ? 2 : 1) bwd_dkdv_
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int dcol = db * 32 + g * 8 + 4 * hg;
-                if constexpr (kDK) {
-                    u32x2 wk;
-                    wk[0] = pack_bf16x2(dkacc[db][4 * g] * p.scale, dkacc[db][4 * g + 1] * p.scale);
-                    wk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * p.scale, dkacc[db][4 * g + 3] * p.scale);
-                    *(u32x2*)(dKr + dcol) = wk;
-                }
-                if constexpr (kDV) {
-                    u32x2 wv;
-                    wv[0] = pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]);
-                    wv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
-                    *(u32x2*)(dVr + dcol) = wv;
-                }
+                u32x2 wk, wv;
+                wk[0] = pack_bf16x2(dkacc[db][4 * g] * p.scale, dkacc[db][4 * g + 1] * p.scale);
+                wk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * p.scale, dkacc[db][4 * g + 3] * p.scale);
+                *(u32x2*)(dKr + dcol) = wk;
+                wv[0] = pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]);
+                wv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
+                *(u32x2*)(dVr + dcol) = wv;
             }
     }
     }   // items
@@ -592,7 +565,11 @@ __device__ __forceinline__ void vmem_wait_n() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-template <int D, int MASK, bool VARLEN = false, int QSPLIT = 1>
+// DQ = false builds the same key-side walk without the dQ part (no dS tile,
+// no mid-step barrier, no atomics): the deterministic mode's dK/dV kernel at
+// d = 128, where the eight-wave split lets dK and dV share one walk at two
+// waves per SIMD.
+template <int D, int MASK, bool VARLEN = false, int QSPLIT = 1, bool DQ = true>
 __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1) bwd_fused_kernel(BwdParams p) {
     constexpr int NW = 4 * QSPLIT;
     constexpr int BKV = 128, BQ = 64, WQ = BQ / QSPLIT;
@@ -605,15 +582,18 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
     constexpr int T_BYTES = BQ * D * 2;
     constexpr int V_OFF = 2 * T_BYTES;
     constexpr int STAGE = V_OFF + 2 * BQ * 4;
-    constexpr int K_OFF = 2 * STAGE;          // K tile [BKV][D], resident for the walk
-    constexpr int DS_OFF = K_OFF + BKV * D * 2;   // dS^T tile [BKV][BQ]
-    constexpr int SMEM = DS_OFF + BKV * BQ * 2;
-    static_assert(K_OFF % 1024 == 0 && DS_OFF % 1024 == 0, "tiles start on 1 KiB");
-    static_assert(QSPLIT == 1 || 4 * NDB * 16 * 64 * 4 <= SMEM, "room for the partial dK / dV");
-    constexpr int kAtomics = 16 * DQB;        // its fp32 dQ values per lane and step
-    // d = 128: K's B operand of S is read from the K tile instead of held in
-    // 32 registers (the kernel would spill otherwise)
+    // d = 128: the B operands of S and dP (K and V of the wave's keys) are
+    // read from K and V tiles kept in LDS for the walk instead of held in 64
+    // registers (the kernel would spill otherwise)
     constexpr bool kKRegs = D == 64 || QSPLIT == 1;
+    constexpr int K_OFF = 2 * STAGE;              // K tile [BKV][D] (dQ's B operand, and S's at d = 128)
+    constexpr int VT_OFF = K_OFF + BKV * D * 2;   // V tile [BKV][D] (d = 128 only)
+    constexpr int DS_OFF = VT_OFF + (kKRegs ? 0 : BKV * D * 2);   // dS^T tile [BKV][BQ]
+    constexpr int SMEM = DQ ? DS_OFF + BKV * BQ * 2 : DS_OFF;
+    static_assert(K_OFF % 1024 == 0 && VT_OFF % 1024 == 0 && DS_OFF % 1024 == 0, "tiles start on 1 KiB");
+    static_assert(SMEM <= 160 * 1024, "LDS of one CU");
+    static_assert(QSPLIT == 1 || 4 * NDB * 16 * 64 * 4 <= SMEM, "room for the partial dK / dV");
+    constexpr int kAtomics = DQ ? 16 * DQB : 0;   // its fp32 dQ values per lane and step
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -639,7 +619,7 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
     const bf16* Kh = (const bf16*)p.k + sg.k_row0 * D;
     const bf16* Vh = (const bf16*)p.v + sg.k_row0 * D;
     const bf16* dOh = (const bf16*)p.dO + sg.q_row0 * D;
-    float* dQa = p.dqacc + sg.q_row0 * D;
+    float* dQa = DQ ? p.dqacc + sg.q_row0 * D : nullptr;
 
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (uint32_t)Nk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, (uint32_t)Nk * D * 2);
@@ -650,6 +630,8 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
     const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
     const uint32_t smem_lds = lds_address(smem);
     const char* ktile = smem + K_OFF;
+    const char* vtile = smem + VT_OFF;
+    const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
     char* dstile = smem + DS_OFF;
 
     // this lane's byte offsets of its dQ block items in a step's rows:
@@ -662,12 +644,13 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
     const int kw = k0 + wk * 32;              // this wave's first key
     const int kj = kw + l32;                  // this lane's key
 
-    // K^T (unless read from the K tile) and V^T as B operands: lane = key
-    bf16x8 kreg[kKRegs ? NKK : 1], vreg[NKK];
+    // K^T and V^T as B operands (lane = key) in registers, or read from the
+    // K and V tiles at d = 128
+    bf16x8 kreg[kKRegs ? NKK : 1], vreg[kKRegs ? NKK : 1];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
+    for (int kk = 0; kk < (kKRegs ? NKK : 0); ++kk) {
         const uint32_t o = (uint32_t)kj * D * 2 + (16 * kk + 8 * hg) * 2;
-        if constexpr (kKRegs) kreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rk, o, 0));
+        kreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rk, o, 0));
         vreg[kk] = __builtin_bit_cast(bf16x8, buf_load128(rv, o, 0));
     }
 
@@ -704,7 +687,8 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
         dvacc[db] = zero16();
     }
 
-    kcopier.issue(rk_w, k0, smem_lds + K_OFF);
+    if (DQ || !kKRegs) kcopier.issue(rk_w, k0, smem_lds + K_OFF);
+    if (!kKRegs) kcopier.issue(rv_w, k0, smem_lds + VT_OFF);
     if (qt0 < n_qt) {
         load_step(qt0, 0);
         if (wave == 0) {
@@ -715,8 +699,8 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
     __builtin_amdgcn_s_waitcnt(0x0F70);
     tile_barrier();
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        if constexpr (kKRegs) mark_loaded(kreg[kk]);
+    for (int kk = 0; kk < (kKRegs ? NKK : 0); ++kk) {
+        mark_loaded(kreg[kk]);
         mark_loaded(vreg[kk]);
     }
 
@@ -735,6 +719,12 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
         }
 
         const bool active = kw < Nk && qa + WQ - 1 >= wq_first && (!kLeft || qa <= wq_last);
+        // d = 128: the lane index, opaque to the compiler once per step, so
+        // the swizzled per-lane operand addresses are formed inside the step
+        // instead of hoisted out of the walk (about 80 of them; kept live
+        // they spill)
+        int ln = lane;
+        if constexpr (!kKRegs) asm volatile("" : "+v"(ln));
         if (active) {
             // ---- S = Q K^T and dP = dO V^T (lane = key, items = queries) ----
             f32x16 s[NQB], dp[NQB];
@@ -747,18 +737,19 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
             for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
-                    const bf16x8 kb = kKRegs ? kreg[kKRegs ? kk : 0] : tile_read_row<D>(ktile, wk * 32, kk, lane);
-                    s[qb] = mfma_bf16(tile_read_row<D>(qs, qw0 + qb * 32, kk, lane), kb, s[qb]);
-                    dp[qb] = mfma_bf16(tile_read_row<D>(dos, qw0 + qb * 32, kk, lane), vreg[kk], dp[qb]);
+                    const bf16x8 kb = kKRegs ? kreg[kKRegs ? kk : 0] : tile_read_row<D>(ktile, wk * 32, kk, ln);
+                    const bf16x8 vb = kKRegs ? vreg[kKRegs ? kk : 0] : tile_read_row<D>(vtile, wk * 32, kk, ln);
+                    s[qb] = mfma_bf16(tile_read_row<D>(qs, qw0 + qb * 32, kk, ln), kb, s[qb]);
+                    dp[qb] = mfma_bf16(tile_read_row<D>(dos, qw0 + qb * 32, kk, ln), vb, dp[qb]);
                 }
             if constexpr (D == 128 && NQB == 1 && !kKRegs) {
-                // the three operand reads of a k-step (Q, dO, K) two k-steps
+                // the four operand reads of a k-step (Q, dO, K, V) two k-steps
                 // ahead of its two MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                    if (kk + 2 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                    if (kk + 2 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
                 }
             }
             // ---- mask: steps that straddle a bound, the query tail or the
@@ -801,7 +792,7 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
             // qc*16 + 4hg + {0..3} (words 0, 1) and qc*16 + 8 + 4hg + {0..3} ----
             const uint32_t krow = (uint32_t)(wk * 32 + l32);
 #pragma unroll
-            for (int qc = 0; qc < NQC; ++qc) {
+            for (int qc = 0; qc < (DQ ? NQC : 0); ++qc) {
                 const uint32_t ch = (uint32_t)(qw0 / 8 + 2 * qc);
                 u32x2 a, b;
                 a[0] = dsw[qc][0];
@@ -816,9 +807,9 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
             for (int qc = 0; qc < NQC; ++qc)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qw0 + qc * 16, db * 32, lane),
+                    dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qw0 + qc * 16, db * 32, ln),
                                           __builtin_bit_cast(bf16x8, pw[qc]), dvacc[db]);
-                    dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qw0 + qc * 16, db * 32, lane),
+                    dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qw0 + qc * 16, db * 32, ln),
                                           __builtin_bit_cast(bf16x8, dsw[qc]), dkacc[db]);
                 }
             if constexpr (D == 128) {   // two transposed reads per MFMA, four ahead
@@ -830,7 +821,7 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
                     if (i < nm - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
                 }
             }
-        } else {
+        } else if constexpr (DQ) {
             // no visible pair for this wave: its part of the dS tile is zero
             const uint32_t krow = (uint32_t)(wk * 32 + l32);
             u32x2 z;
@@ -842,20 +833,20 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
                 *(u32x2*)(dstile + tile_offset<BQ>(krow, ch + 1) + 8 * hg) = z;
             }
         }
-        tile_barrier();   // the whole dS tile is written
+        if constexpr (DQ) tile_barrier();   // the whole dS tile is written
 
         // ---- dQ block += dS K over the tile's 128 keys, added to the fp32
         // buffer (rows q0 .. q0+63; rows past Nq are outside the range) ----
-        {
+        if constexpr (DQ) {
             f32x16 dq[DQB];
 #pragma unroll
             for (int b = 0; b < DQB; ++b) dq[b] = zero16();
 #pragma unroll
             for (int kc = 0; kc < BKV / 16; ++kc) {
-                const bf16x8 a = tile_read_tr<BQ>(dstile, kc * 16, dq_qb * 32, lane);
+                const bf16x8 a = tile_read_tr<BQ>(dstile, kc * 16, dq_qb * 32, ln);
 #pragma unroll
                 for (int b = 0; b < DQB; ++b)
-                    dq[b] = mfma_bf16(a, tile_read_tr<D>(ktile, kc * 16, (dq_db + b) * 32, lane), dq[b]);
+                    dq[b] = mfma_bf16(a, tile_read_tr<D>(ktile, kc * 16, (dq_db + b) * 32, ln), dq[b]);
             }
             const __amdgpu_buffer_rsrc_t rdq =
                 make_rsrc(dQa + (size_t)q0 * D, (uint32_t)(min(BQ, Nq - q0) * D * 4));
@@ -968,24 +959,26 @@ __global__ void __launch_bounds__(256) bwd_dq_convert_kernel(const float* acc, b
 }
 
 // ---------------------------------------------------------------------------
-// part: -1 the dQ kernel, 0/1/2 the key-side kernel's PART
+// Deterministic mode.  keyside = false: the dQ kernel; true: the key-side
+// kernel (bwd_dkdv_kernel at d = 64, bwd_fused_kernel without its dQ part
+// at d = 128).
 template <int D, int MASK, bool VARLEN>
-static const void* bwd_kernel_m(int part) {
-    if (part < 0) return (const void*)bwd_dq_kernel<D, MASK, VARLEN>;
-    if constexpr (D == 64) return (const void*)bwd_dkdv_kernel<D, MASK, VARLEN, 0>;
-    else return part == 1 ? (const void*)bwd_dkdv_kernel<D, MASK, VARLEN, 1> : (const void*)bwd_dkdv_kernel<D, MASK, VARLEN, 2>;
+static const void* bwd_kernel_m(bool keyside) {
+    if (!keyside) return (const void*)bwd_dq_kernel<D, MASK, VARLEN>;
+    if constexpr (D == 64) return (const void*)bwd_dkdv_kernel<D, MASK, VARLEN>;
+    else return (const void*)bwd_fused_kernel<D, MASK, VARLEN, 2, false>;
 }
 
 template <int D, bool VARLEN>
-static const void* bwd_kernel(int part, int mask) {
-    if (mask == kMaskCausal) return bwd_kernel_m<D, kMaskCausal, VARLEN>(part);
-    if (mask == kMaskWindow) return bwd_kernel_m<D, kMaskWindow, VARLEN>(part);
-    return bwd_kernel_m<D, kMaskNone, VARLEN>(part);
+static const void* bwd_kernel(bool keyside, int mask) {
+    if (mask == kMaskCausal) return bwd_kernel_m<D, kMaskCausal, VARLEN>(keyside);
+    if (mask == kMaskWindow) return bwd_kernel_m<D, kMaskWindow, VARLEN>(keyside);
+    return bwd_kernel_m<D, kMaskNone, VARLEN>(keyside);
 }
 
 template <int D>
-static const void* bwd_kernel(int part, int mask, bool varlen) {
-    return varlen ? bwd_kernel<D, true>(part, mask) : bwd_kernel<D, false>(part, mask);
+static const void* bwd_kernel(bool keyside, int mask, bool varlen) {
+    return varlen ? bwd_kernel<D, true>(keyside, mask) : bwd_kernel<D, false>(keyside, mask);
 }
 
 template <int D>
@@ -993,19 +986,19 @@ static hipError_t launch_bwd_d(int mask, bool varlen, const BwdParams& p, hipStr
     BwdParams pp = p;
     void* args[] = {&pp};
     // dQ first: it also writes every query row's D and LSE * log2(e) to the
-    // workspace, which the dK/dV kernel reads (stream order)
+    // workspace, which the key-side kernel reads (stream order)
     const long grid_q = (long)p.BH * p.q_slots;
     if (grid_q > 0) {   // with Nk == 0 every row is empty and dQ = 0 is written
-        const void* fn = bwd_kernel<D>(-1, mask, varlen);
-        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_q), dim3(256), args, 0, s);
+        hipError_t e = hipLaunchKernel(bwd_kernel<D>(false, mask, varlen), dim3((unsigned)grid_q), dim3(256),
+                                       args, 0, s);
         if (e != hipSuccess) return e;
     }
-    const long grid_kv = (long)p.BH * p.kv_slots;
     // with Nq == 0 the walk is empty and dK = dV = 0 are written; d = 128:
-    // the dV kernel, then the dK kernel
-    for (int part = D == 64 ? 0 : 1; grid_kv > 0 && part <= (D == 64 ? 0 : 2); ++part) {
-        const void* fn = bwd_kernel<D>(part, mask, varlen);
-        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(256), args, 0, s);
+    // eight waves per workgroup, two per 32-key slice
+    const long grid_kv = (long)p.BH * p.kv_slots;
+    if (grid_kv > 0) {
+        hipError_t e = hipLaunchKernel(bwd_kernel<D>(true, mask, varlen), dim3((unsigned)grid_kv),
+                                       dim3(D == 64 ? 256 : 512), args, 0, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1020,10 +1013,7 @@ bool bwd_pair_tiles(bool causal, long bh, int n_tiles) {
 
 template <int D, bool VARLEN>
 static const void* bwd_fused(int mask) {
-#ifndef FA_BWD128_QSPLIT
-#define FA_BWD128_QSPLIT 2
-#endif
-    constexpr int QS = D == 64 ? 1 : FA_BWD128_QSPLIT;
+    constexpr int QS = D == 64 ? 1 : 2;
     if (mask == kMaskCausal) return (const void*)bwd_fused_kernel<D, kMaskCausal, VARLEN, QS>;
     if (mask == kMaskWindow) return (const void*)bwd_fused_kernel<D, kMaskWindow, VARLEN, QS>;
     return (const void*)bwd_fused_kernel<D, kMaskNone, VARLEN, QS>;
@@ -1046,8 +1036,7 @@ static hipError_t launch_bwd_atomic_d(int mask, bool varlen, const BwdParams& p,
     if (grid_kv > 0) {
         void* args[] = {&pp};
         const void* fn = varlen ? bwd_fused<D, true>(mask) : bwd_fused<D, false>(mask);
-        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(D == 64 ? 256 : 256 * FA_BWD128_QSPLIT),
-                                       args, 0, s);
+        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_kv), dim3(D == 64 ? 256 : 512), args, 0, s);
         if (e != hipSuccess) return e;
     }
     if (rows > 0) {
