@@ -165,7 +165,12 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, in
  *                      rate (about 3.2e11 adds/s on MI355X): at B=4 H=16
  *                      N=4096 d=64 causal that is 2.8e8 adds, >= 0.86 ms,
  *                      where the deterministic mode takes about 0.52 ms.
- * Both modes meet the same tolerance against the exact gradients.
+ * Both modes meet the same tolerance against the exact gradients.  D is
+ * formed once per row in float32 from the bf16 dO and O; the key-side
+ * products use it as float32, while the deterministic dQ kernel folds -D into
+ * its dP product as a pair of bf16 values whose sum is -D within 2^-16
+ * relative (one more MFMA k-step instead of a subtraction per score), so
+ * dQ and dK see D to within that rounding.
  *
  * Only FA_BF16 is accepted (FA_ERR_DTYPE otherwise).  Calls that share a
  * workspace must not overlap.
