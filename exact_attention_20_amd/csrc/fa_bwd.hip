@@ -630,13 +630,36 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
     const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
     const uint32_t smem_lds = lds_address(smem);
     const char* ktile = smem + K_OFF;
-    const char* vtile = smem + VT_OFF;
     const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
     char* dstile = smem + DS_OFF;
 
     // this lane's byte offsets of its dQ block items in a step's rows:
     // item 4g+e is query 32*dq_qb + 8g + 4hg + e, column 32*dq_db + l32
     const uint32_t dq_off0 = (uint32_t)(((dq_qb * 32 + 4 * hg) * D + dq_db * 32 + l32) * 4);
+
+    // d = 128: every operand read is one of these per-lane offsets plus an
+    // immediate (the stage, the tile, the k-step's rows).  The swizzle of a
+    // row depends on its index mod 16 only, and every tile row block starts
+    // on a multiple of 16, so a row read of rows r0 + l32 is r0 * 2D bytes
+    // plus the offset of row l32, and likewise for the transposed reads.
+    uint32_t qrow[NKK], kvrow[NKK], trq[2 * NDB];
+    if constexpr (!kKRegs) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const uint32_t r = tile_offset<D>((uint32_t)l32, (uint32_t)(2 * kk + hg));
+            qrow[kk] = (uint32_t)(qw0 * D * 2) + r;                 // rows qw0 + l32 of a stage tile
+            kvrow[kk] = (uint32_t)(K_OFF + wk * 32 * D * 2) + r;    // rows wk*32 + l32 of the K tile
+        }
+        const uint32_t gi = lane & 15;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t row = 4 * hg + (gi >> 2) + 8 * h;
+                const uint32_t col = db * 32 + (lane & 16) + 4 * (gi & 3);
+                trq[2 * db + h] = (uint32_t)(qw0 * D * 2) + tile_offset<D>(row, col >> 3) + (col & 4) * 2;
+            }
+    }
 
     for (int it = 0; it < n_items; ++it) {
     const int kt = it == 0 ? slot : n_kt - 1 - slot;
@@ -704,8 +727,11 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
         mark_loaded(vreg[kk]);
     }
 
-    for (int qt = qt0; qt < n_qt; ++qt) {
-        const int st = (qt - qt0) & 1;
+    // The walk, unrolled by two so that the stage buffer of a step is a
+    // compile-time constant (its operand addresses then take it as an
+    // immediate offset).
+    auto walk_step = [&](const int qt, auto stage_c) {
+        constexpr int st = decltype(stage_c)::value;
         const char* qs = smem + st * STAGE;
         const char* dos = qs + T_BYTES;
         const float* l2s = (const float*)(qs + V_OFF);
@@ -719,12 +745,8 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
         }
 
         const bool active = kw < Nk && qa + WQ - 1 >= wq_first && (!kLeft || qa <= wq_last);
-        // d = 128: the lane index, opaque to the compiler once per step, so
-        // the swizzled per-lane operand addresses are formed inside the step
-        // instead of hoisted out of the walk (about 80 of them; kept live
-        // they spill)
-        int ln = lane;
-        if constexpr (!kKRegs) asm volatile("" : "+v"(ln));
+        const int ln = lane;
+        const char* sb = smem + st * STAGE;   // this step's stage (an immediate)
         if (active) {
             // ---- S = Q K^T and dP = dO V^T (lane = key, items = queries) ----
             f32x16 s[NQB], dp[NQB];
@@ -737,10 +759,15 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
             for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
-                    const bf16x8 kb = kKRegs ? kreg[kKRegs ? kk : 0] : tile_read_row<D>(ktile, wk * 32, kk, ln);
-                    const bf16x8 vb = kKRegs ? vreg[kKRegs ? kk : 0] : tile_read_row<D>(vtile, wk * 32, kk, ln);
-                    s[qb] = mfma_bf16(tile_read_row<D>(qs, qw0 + qb * 32, kk, ln), kb, s[qb]);
-                    dp[qb] = mfma_bf16(tile_read_row<D>(dos, qw0 + qb * 32, kk, ln), vb, dp[qb]);
+                    if constexpr (kKRegs) {
+                        s[qb] = mfma_bf16(tile_read_row<D>(qs, qw0 + qb * 32, kk, ln), kreg[kk], s[qb]);
+                        dp[qb] = mfma_bf16(tile_read_row<D>(dos, qw0 + qb * 32, kk, ln), vreg[kk], dp[qb]);
+                    } else {   // NQB = 1
+                        const bf16x8 kb = *(const bf16x8*)(smem + kvrow[kk]);
+                        const bf16x8 vb = *(const bf16x8*)(smem + (VT_OFF - K_OFF) + kvrow[kk]);
+                        s[qb] = mfma_bf16(*(const bf16x8*)(sb + qrow[kk]), kb, s[qb]);
+                        dp[qb] = mfma_bf16(*(const bf16x8*)(sb + T_BYTES + qrow[kk]), vb, dp[qb]);
+                    }
                 }
             if constexpr (D == 128 && NQB == 1 && !kKRegs) {
                 // the four operand reads of a k-step (Q, dO, K, V) two k-steps
@@ -807,10 +834,18 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
             for (int qc = 0; qc < NQC; ++qc)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qw0 + qc * 16, db * 32, ln),
-                                          __builtin_bit_cast(bf16x8, pw[qc]), dvacc[db]);
-                    dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qw0 + qc * 16, db * 32, ln),
-                                          __builtin_bit_cast(bf16x8, dsw[qc]), dkacc[db]);
+                    bf16x8 dot, qt_op;
+                    if constexpr (kKRegs) {
+                        dot = tile_read_tr<D>(dos, qw0 + qc * 16, db * 32, ln);
+                        qt_op = tile_read_tr<D>(qs, qw0 + qc * 16, db * 32, ln);
+                    } else {
+                        const char* d0 = sb + T_BYTES + qc * 16 * D * 2;
+                        const char* q0p = sb + qc * 16 * D * 2;
+                        dot = concat8(lds_read_tr16(d0 + trq[2 * db]), lds_read_tr16(d0 + trq[2 * db + 1]));
+                        qt_op = concat8(lds_read_tr16(q0p + trq[2 * db]), lds_read_tr16(q0p + trq[2 * db + 1]));
+                    }
+                    dvacc[db] = mfma_bf16(dot, __builtin_bit_cast(bf16x8, pw[qc]), dvacc[db]);
+                    dkacc[db] = mfma_bf16(qt_op, __builtin_bit_cast(bf16x8, dsw[qc]), dkacc[db]);
                 }
             if constexpr (D == 128) {   // two transposed reads per MFMA, four ahead
                 constexpr int nm = 2 * NQC * NDB;
@@ -868,6 +903,10 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
         mark_loaded(nl2);
         mark_loaded(ndd);
         tile_barrier();
+    };
+    for (int qt = qt0; qt < n_qt; qt += 2) {
+        walk_step(qt, std::integral_constant<int, 0>{});
+        if (qt + 1 < n_qt) walk_step(qt + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- QSPLIT > 1: sum the slice's partial dK^T, dV^T through LDS (the
