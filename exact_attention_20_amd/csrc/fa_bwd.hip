@@ -181,8 +181,27 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
         mark_loaded(vreg[kk]);
     }
 
-    for (int qt = qt0; qt < n_qt; ++qt) {
-        const int st = (qt - qt0) & 1;
+    // Operand reads are per-lane offsets formed once plus immediates (the
+    // stage, Q or dO, the query block, the k-step's rows; a row's swizzle
+    // depends on its index mod 16 only); the walk is unrolled by two so the
+    // stage is a constant.
+    uint32_t rowoff[NKK], trq[2 * NDB];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) rowoff[kk] = tile_offset<D>((uint32_t)l32, (uint32_t)(2 * kk + hg));
+    {
+        const uint32_t gi = lane & 15;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t row = 4 * hg + (gi >> 2) + 8 * h;
+                const uint32_t col = db * 32 + (lane & 16) + 4 * (gi & 3);
+                trq[2 * db + h] = tile_offset<D>(row, col >> 3) + (col & 4) * 2;
+            }
+    }
+
+    auto walk_step = [&](const int qt, auto stage_c) {
+        constexpr int st = decltype(stage_c)::value;
         const char* qs = smem + st * STAGE;
         const char* dos = qs + T_BYTES;
         const float* l2s = (const float*)(qs + V_OFF);
@@ -206,8 +225,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
             for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
-                    s[qb] = mfma_bf16(tile_read_row<D>(qs, qb * 32, kk, lane), kreg[kk], s[qb]);
-                    dp[qb] = mfma_bf16(tile_read_row<D>(dos, qb * 32, kk, lane), vreg[kk], dp[qb]);
+                    s[qb] = mfma_bf16(*(const bf16x8*)(qs + qb * 32 * D * 2 + rowoff[kk]), kreg[kk], s[qb]);
+                    dp[qb] = mfma_bf16(*(const bf16x8*)(dos + qb * 32 * D * 2 + rowoff[kk]), vreg[kk], dp[qb]);
                 }
             // (the compiler's own order of the operand reads: an explicit
             // four-ahead order measured 1.8% slower at d = 64)
@@ -256,10 +275,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
             for (int qc = 0; qc < NQC; ++qc) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    dvacc[db] = mfma_bf16(tile_read_tr<D>(dos, qc * 16, db * 32, lane),
-                                          __builtin_bit_cast(bf16x8, pw[qc]), dvacc[db]);
-                    dkacc[db] = mfma_bf16(tile_read_tr<D>(qs, qc * 16, db * 32, lane),
-                                          __builtin_bit_cast(bf16x8, dsw[qc]), dkacc[db]);
+                    const char* dr = dos + qc * 16 * D * 2;
+                    const char* qr = qs + qc * 16 * D * 2;
+                    const bf16x8 dot = concat8(lds_read_tr16(dr + trq[2 * db]), lds_read_tr16(dr + trq[2 * db + 1]));
+                    const bf16x8 qto = concat8(lds_read_tr16(qr + trq[2 * db]), lds_read_tr16(qr + trq[2 * db + 1]));
+                    dvacc[db] = mfma_bf16(dot, __builtin_bit_cast(bf16x8, pw[qc]), dvacc[db]);
+                    dkacc[db] = mfma_bf16(qto, __builtin_bit_cast(bf16x8, dsw[qc]), dkacc[db]);
                 }
             }
         }
@@ -273,6 +294,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
         mark_loaded(nl2);
         mark_loaded(ndd);
         tile_barrier();
+    };
+    for (int qt = qt0; qt < n_qt; qt += 2) {
+        walk_step(qt, std::integral_constant<int, 0>{});
+        if (qt + 1 < n_qt) walk_step(qt + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- dK = scale * dK^T, dV = dV^T (lane = key, items = d) ----
@@ -418,13 +443,32 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     }
     const bf16x8 ones_a = __builtin_bit_cast(bf16x8, ones_w), negd_b = __builtin_bit_cast(bf16x8, negd_w);
 
-    for (int t = t_first; t < ntiles; ++t) {
+    // Operand reads are per-lane offsets formed once plus immediates (the
+    // buffer, K or V, the key block, the k-step's rows): the swizzle of a row
+    // depends on its index mod 16 only, and every block starts on a multiple
+    // of 16.  The tile loop is unrolled by two so the buffer is a constant.
+    uint32_t rowoff[NKK], trk[2 * NDB];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) rowoff[kk] = tile_offset<D>((uint32_t)l32, (uint32_t)(2 * kk + hg));
+    {
+        const uint32_t gi = lane & 15;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t row = 4 * hg + (gi >> 2) + 8 * h;
+                const uint32_t col = db * 32 + (lane & 16) + 4 * (gi & 3);
+                trk[2 * db + h] = tile_offset<D>(row, col >> 3) + (col & 4) * 2;
+            }
+    }
+
+    auto tile_step = [&](const int t, auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
         const int k0 = t * BC;
-        const int buf = (t - t_first) & 1;
         const char* kbuf = smem + buf * BUF_BYTES;
         const char* vbuf = kbuf + T_BYTES;
         const bool has_next = t + 1 < ntiles;
-        if (has_next) load_tile(k0 + BC, (t + 1 - t_first) & 1);
+        if (has_next) load_tile(k0 + BC, buf ^ 1);
 
         if (k0 < kend_w && (!kLeft || k0 + BC > kbeg_w)) {
             // ---- S^T = K Q^T, dP^T = V dO^T (lane = query, items = keys) ----
@@ -438,8 +482,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
             for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    s[kb] = mfma_bf16(tile_read_row<D>(kbuf, kb * 32, kk, lane), qreg[kk], s[kb]);
-                    dp[kb] = mfma_bf16(tile_read_row<D>(vbuf, kb * 32, kk, lane), doreg[kk], dp[kb]);
+                    s[kb] = mfma_bf16(*(const bf16x8*)(kbuf + kb * 32 * D * 2 + rowoff[kk]), qreg[kk], s[kb]);
+                    dp[kb] = mfma_bf16(*(const bf16x8*)(vbuf + kb * 32 * D * 2 + rowoff[kk]), doreg[kk], dp[kb]);
                 }
             // operand reads four ahead of the MFMAs at d = 128, as in dK/dV
             if constexpr (D == 128) {
@@ -489,8 +533,11 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
             for (int kc = 0; kc < NKC; ++kc) {
                 const bf16x8 sb = __builtin_bit_cast(bf16x8, dsw[kc]);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dqacc[db] = mfma_bf16(tile_read_tr<D>(kbuf, kc * 16, db * 32, lane), sb, dqacc[db]);
+                for (int db = 0; db < NDB; ++db) {
+                    const char* kr = kbuf + kc * 16 * D * 2;
+                    const bf16x8 kt = concat8(lds_read_tr16(kr + trk[2 * db]), lds_read_tr16(kr + trk[2 * db + 1]));
+                    dqacc[db] = mfma_bf16(kt, sb, dqacc[db]);
+                }
             }
             if constexpr (D == 128) {   // two transposed reads per MFMA
                 constexpr int nm = NKC * NDB;
@@ -505,6 +552,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
 
         if (has_next) vmem_wait_all();
         tile_barrier();
+    };
+    for (int t = t_first; t < ntiles; t += 2) {
+        tile_step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- dQ = scale * dQ^T (lane = query, items = d) ----
