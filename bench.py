@@ -458,7 +458,16 @@ def bench_varlen(fa, wl, w, args) -> dict:
         if st != 0:
             raise fa.FAError(st, "fa_fwd_varlen")
 
-    ms = time_launches(step, stream, args.steps, args.warmup)
+    # the ceilings first, as in the fixed-length line (they take the chip
+    # through its clock transient before the warm-up)
+    gc = None
+    if not args.no_gemm_ceiling:
+        gc = gemm_ceiling()
+        gc["probe"] = mfma_probe()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms, samples = timed_launches(step, stream, args.steps)
     pairs = sum(visible_pairs(n, n, w.causal) for n in L)
     flops = 4 * w.d * pairs * w.H
     tflops = flops / (ms * 1e-3) / 1e12
@@ -476,33 +485,41 @@ def bench_varlen(fa, wl, w, args) -> dict:
                      "traffic": traffic_for(w.name)},
         "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "peak_GBps": 8000.0, "note": "algorithmic bytes / launch time, warm caches"},
+        "samples": {**samples, "note": "per-launch HIP events inside the timed region"},
+        "device": device_description(),
     }
-    if not args.no_gemm_ceiling:
-        gc = gemm_ceiling()
+    if gc is not None:
         gc["value_over_gemm"] = round(tflops / gc["tflops"], 4)
+        gc["probe"]["value_over_probe"] = round(tflops / gc["probe"]["tflops"], 4)
         result["mfma_ceiling"] = gc
     if not args.no_train_step:
-        # fa_bwd_varlen on the same packed batch (dO drawn after the inputs)
+        # fa_bwd_varlen on the same packed batch (dO drawn after the inputs),
+        # deterministic mode then atomic mode
         g = torch.Generator(device="cpu").manual_seed(w.seed + 1)
         do = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-        need = fa.fa_bwd_varlen_workspace_bytes(w.H, T, w.d, fa.FA_BF16, 0)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
         step()
-        bargv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                 do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()) + argv[5:17] + \
-                (fa.FA_BF16, 0, ws.data_ptr(), need, stream.cuda_stream)
+        bwd_ms = {}
+        for det in (1, 0):
+            need = fa.fa_bwd_varlen_workspace_bytes(w.H, T, w.d, fa.FA_BF16, det)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            bargv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()) + argv[5:17] + \
+                    (fa.FA_BF16, det, ws.data_ptr(), need, stream.cuda_stream)
 
-        def bwd():
-            st = fa.fa_bwd_varlen(*bargv)
-            if st != 0:
-                raise fa.FAError(st, "fa_bwd_varlen")
+            def bwd():
+                st = fa.fa_bwd_varlen(*bargv)
+                if st != 0:
+                    raise fa.FAError(st, "fa_bwd_varlen")
 
-        ms_b = time_launches(bwd, stream, 20, 5)
-        result["backward"] = {"bwd_ms": round(ms_b, 5),
-                              "bwd_tflops": round(10 * w.d * pairs * w.H / ms_b / 1e9, 3),
-                              "note": "fa_bwd_varlen, fast mode (pre-pass, key-side kernel with dQ "
-                                      "atomics, dQ conversion); 10*d FLOPs per visible pair"}
+            bwd_ms[det] = time_launches(bwd, stream, 20, 5)
+            del ws
+        result["backward"] = {"bwd_ms": round(bwd_ms[1], 5),
+                              "bwd_tflops": round(10 * w.d * pairs * w.H / bwd_ms[1] / 1e9, 3),
+                              "bwd_atomic_ms": round(bwd_ms[0], 5),
+                              "bwd_atomic_tflops": round(10 * w.d * pairs * w.H / bwd_ms[0] / 1e9, 3),
+                              "note": "fa_bwd_varlen: deterministic mode (dQ kernel + key-side kernel), "
+                                      "then the atomic mode; 10*d FLOPs per visible pair"}
     if not args.no_cpu_baseline:
         from oracle import attention_forward
         # whole (head, sequence) pairs, head by head, until ~15 s of CPU work

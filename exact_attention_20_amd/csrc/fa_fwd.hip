@@ -320,7 +320,10 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
             // priority is raised while this wave feeds the matrix cores, so
             // the other wave of the SIMD takes the issue slots they leave.
             __builtin_amdgcn_s_setprio(1);
-            float rs[4] = {0.f, 0.f, 0.f, 0.f};   // fp32 row sums in four chains
+            // fp32 row sums in four chains, each started with its first value
+            // (P >= +0, so this equals adding it to 0, which the compiler
+            // cannot fold away because of signed zeros)
+            float rs[4];
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
                 const int kb = kc >> 1, i0 = (kc & 1) * 8;
@@ -329,8 +332,13 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
                 for (int j = 0; j < 4; ++j) {
                     const float p0 = exp2_hw(fmaf(s[kb][i0 + 2 * j], p.scale_log2, nbase));
                     const float p1 = exp2_hw(fmaf(s[kb][i0 + 2 * j + 1], p.scale_log2, nbase));
-                    rs[(2 * j) & 3] += p0;
-                    rs[(2 * j + 1) & 3] += p1;
+                    if (kc == 0 && j < 2) {
+                        rs[2 * j] = p0;
+                        rs[2 * j + 1] = p1;
+                    } else {
+                        rs[(2 * j) & 3] += p0;
+                        rs[(2 * j + 1) & 3] += p1;
+                    }
                     w[j] = pack_bf16x2(p0, p1);
                 }
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
@@ -340,8 +348,8 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
                                          pb, oacc[db]);
             }
             l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-            // Issue order: the first block's 28 VALU instructions (8 FMA, 8
-            // exp, 8 adds, 4 packs) and two V^T operands (four transposed
+            // Issue order: the first block's 24 VALU instructions (8 FMA, 8
+            // exp, 4 adds, 4 packs) and two V^T operands (four transposed
             // reads), then per MFMA two transposed reads and 7*4/NDB of the
             // next block's VALU instructions.  Measured against the compiler's
             // own order (all exponentials, then P.V in bursts of eight reads):
@@ -349,7 +357,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
             // training-step forward, -1.3% at N = 32768.
             {
                 constexpr int vAhead = 2;
-                __builtin_amdgcn_sched_group_barrier(0x002, 28, 1);
+                __builtin_amdgcn_sched_group_barrier(0x002, 24, 1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * vAhead, 1);
 #pragma unroll
                 for (int i = 0; i < NKC * NDB; ++i) {
