@@ -2,6 +2,11 @@
 MFMA throughput probe libfa_probe.so that bench.py reports beside the roofline.
 
     python -m exact_attention_20_amd.build
+    python -m exact_attention_20_amd.build --resource-usage [out.md]
+
+The second form compiles the kernel sources for the device only with the
+compiler's kernel-resource-usage remarks and prints, per instantiated kernel,
+its VGPRs, AGPRs, spills, scratch, LDS and occupancy as a markdown table.
 
 Every HIP source is compiled with packed-FP32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass prints
@@ -71,5 +76,76 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+_FIELDS = (
+    ("VGPRs", "VGPRs"),
+    ("AGPRs", "AGPRs"),
+    ("VGPRs Spill", "VGPR spill"),
+    ("SGPRs Spill", "SGPR spill"),
+    ("ScratchSize [bytes/lane]", "scratch B/lane"),
+    ("LDS Size [bytes/block]", "LDS B/block"),
+    ("Occupancy [waves/SIMD]", "waves/SIMD"),
+)
+
+
+def _demangle(names):
+    tool = shutil.which("llvm-cxxfilt") or shutil.which("c++filt")
+    if tool is None:
+        return list(names)
+    out = subprocess.run([tool], input="\n".join(names), capture_output=True, text=True, check=True)
+    return out.stdout.splitlines()
+
+
+def parse_remarks(text: str):
+    """Split the compiler's kernel-resource-usage remarks into one dict per
+    kernel: ``_name`` (mangled) plus each ``key: value`` remark after it."""
+    rows, cur = [], None
+    for line in text.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split("[-Rpass-analysis", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            cur = {"_name": body.split(":", 1)[1].strip()}
+            rows.append(cur)
+        elif cur is not None and ":" in body:
+            key, val = body.rsplit(":", 1)
+            cur[key.strip()] = val.strip()
+    return rows
+
+
+def resource_usage(sources=("fa_fwd.hip", "fa_bwd.hip")):
+    """Per-kernel register, spill, LDS and occupancy figures from the compiler.
+
+    Returns a list of ``(source, kernel, {field: value})`` in the order the
+    compiler reports them.
+    """
+    cc = hipcc()
+    rows = []
+    for src in sources:
+        cmd = [cc, *flags(), "-x", "hip", "--cuda-device-only", "-c", os.path.join(CSRC, src),
+               "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+        res = subprocess.run(cmd, capture_output=True, text=True, check=True)
+        rows += [(src, r) for r in parse_remarks(res.stderr)]
+    names = _demangle([r["_name"] for _, r in rows])
+    return [(src, name, r) for (src, r), name in zip(rows, names)]
+
+
+def resource_table(rows) -> str:
+    head = "| source | kernel | " + " | ".join(h for _, h in _FIELDS) + " |"
+    sep = "|" + "---|" * (2 + len(_FIELDS))
+    out = [head, sep]
+    for src, name, r in rows:
+        name = name.replace("void ", "", 1).split("(", 1)[0].replace("fa::", "")
+        out.append(f"| {src} | `{name}` | " + " | ".join(r.get(k, "") for k, _ in _FIELDS) + " |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--resource-usage" in sys.argv:
+        table = resource_table(resource_usage())
+        rest = [a for a in sys.argv[1:] if a != "--resource-usage"]
+        if rest:
+            with open(rest[0], "w") as f:
+                f.write(table + "\n")
+        print(table)
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -294,3 +294,35 @@ def test_varlen_workspace_bytes():
         assert ws(-1, 3, 64, fa.FA_BF16, det) == 0
     # more rows per head than FA_MAX_SEQ are fine when packed
     assert ws(2, 1 << 24, 64, fa.FA_BF16, 1) == 2 * 2 * (1 << 24) * 4
+
+
+_REMARKS = """\
+src.hip:87:1: remark: Function Name: _ZN2fa15fwd_bf16_kernelILi64ELi1ELb0ELb0EEEvNS_9FwdParamsE [-Rpass-analysis=kernel-resource-usage]
+src.hip:87:1: remark:     TotalSGPRs: 106 [-Rpass-analysis=kernel-resource-usage]
+src.hip:87:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]
+src.hip:87:1: remark:     AGPRs: 0 [-Rpass-analysis=kernel-resource-usage]
+src.hip:87:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+src.hip:87:1: remark:     Occupancy [waves/SIMD]: 4 [-Rpass-analysis=kernel-resource-usage]
+src.hip:87:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+src.hip:87:1: remark:     LDS Size [bytes/block]: 32784 [-Rpass-analysis=kernel-resource-usage]
+some unrelated warning line
+src.hip:624:1: remark: Function Name: _ZN2fa13bwd_dq_kernelILi128ELi1ELb0EEEvNS_9BwdParamsE [-Rpass-analysis=kernel-resource-usage]
+src.hip:624:1: remark:     VGPRs: 252 [-Rpass-analysis=kernel-resource-usage]
+src.hip:624:1: remark:     VGPRs Spill: 4 [-Rpass-analysis=kernel-resource-usage]
+"""
+
+
+def test_resource_usage_remark_parser():
+    """The compiler's per-kernel resource remarks become one row per kernel."""
+    from exact_attention_20_amd import build
+
+    rows = build.parse_remarks(_REMARKS)
+    assert [r["_name"] for r in rows] == [
+        "_ZN2fa15fwd_bf16_kernelILi64ELi1ELb0ELb0EEEvNS_9FwdParamsE",
+        "_ZN2fa13bwd_dq_kernelILi128ELi1ELb0EEEvNS_9BwdParamsE",
+    ]
+    assert rows[0]["VGPRs"] == "128" and rows[0]["LDS Size [bytes/block]"] == "32784"
+    assert rows[0]["Occupancy [waves/SIMD]"] == "4" and rows[0]["ScratchSize [bytes/lane]"] == "0"
+    assert rows[1]["VGPRs Spill"] == "4" and "AGPRs" not in rows[1]
+    table = build.resource_table([("a.hip", "void fa::k<64, 1>(fa::FwdParams)", rows[0])])
+    assert "| a.hip | `k<64, 1>` | 128 | 0 | 0 |" in table
