@@ -323,11 +323,12 @@ def attention_forward_splitkv(q, k, v, scale=None, causal=False, n_splits=0, wor
 
 def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=None,
                        window=None, deterministic=True):
-    """dq, dk, dv of sum(do * o) via fa_bwd, or fa_bwd_window (bf16 only).
+    """dq, dk, dv of sum(do * o) via fa_bwd, or fa_bwd_window (bf16 or fp32).
     ``o`` and ``lse`` are the outputs of ``attention_forward`` for the same
     inputs and mask.  ``deterministic`` (the default, and the faster mode on
     MI355X) runs the bitwise-repeatable kernels; False runs the single
-    key-side kernel that sums dQ with fp32 atomics."""
+    key-side kernel that sums dQ with fp32 atomics (bf16 only: fp32 inputs
+    always take the deterministic kernels)."""
     import torch
     B, H, Nq, d = q.shape
     Nk = k.shape[2]

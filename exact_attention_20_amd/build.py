@@ -27,7 +27,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = os.environ.get("FA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_noalloc.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_f32.hip", "fa_noalloc.hip"]
 
 
 def hipcc() -> str:
@@ -112,7 +112,7 @@ def parse_remarks(text: str):
     return rows
 
 
-def resource_usage(sources=("fa_fwd.hip", "fa_bwd.hip")):
+def resource_usage(sources=("fa_fwd.hip", "fa_bwd.hip", "fa_bwd_f32.hip")):
     """Per-kernel register, spill, LDS and occupancy figures from the compiler.
 
     Returns a list of ``(source, kernel, {field: value})`` in the order the

@@ -178,7 +178,8 @@ int fa::bwd_check_args(const void* q, const void* k, const void* v, const void* 
     *work = false;
     const int st = check_common(B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
-    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    // the key-side grid (64- or 128-key tiles) must fit in 32 bits as well
+    if ((long double)B * H * ((Nk + 63) / 64 + 1) > 2.0e9L) return FA_ERR_SHAPE;
     if ((long)B * H == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
     const bool has_q = Nq > 0, has_k = Nk > 0;
     if ((has_q && (!q || !o || !lse || !dO || !dq)) || (has_k && (!k || !v || !dk || !dv))) return FA_ERR_NULL;
@@ -203,8 +204,8 @@ size_t bwd_ws_bytes(size_t rows, int d, int deterministic) {
 
 extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int deterministic) {
     if (check_common(B, H, Nq, Nk, d, 1.0f, dtype) != FA_OK) return 0;
-    if (dtype != FA_BF16) return 0;
-    return bwd_ws_bytes((size_t)B * H * Nq, d, deterministic);
+    // fp32 has one (deterministic) algorithm whatever the argument says
+    return bwd_ws_bytes((size_t)B * H * Nq, d, deterministic || dtype == FA_F32);
 }
 
 namespace {
@@ -239,16 +240,22 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o,
     p.Nq = Nq;
     p.Nk = Nk;
     p.BH = (int)BH;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.44269504088896340736f;
+    p.wl = mask.wl;
+    p.wr = mask.wr;
+    if (dtype == FA_F32) {
+        p.dqacc = nullptr;
+        p.q_slots = (Nq + 63) / 64;
+        p.kv_slots = (Nk + 63) / 64;
+        return hip_status(fa::launch_bwd_f32(d, mask.mode, p, (hipStream_t)stream));
+    }
     const int n_kt = (Nk + 127) / 128, n_qt = (Nq + 127) / 128;
     const bool causal = mask.mode == fa::kMaskCausal;
     p.kv_paired = fa::bwd_pair_tiles(causal, BH, n_kt) ? 1 : 0;
     p.kv_slots = p.kv_paired ? (n_kt + 1) / 2 : n_kt;
     p.q_paired = fa::bwd_pair_tiles(causal, BH, n_qt) ? 1 : 0;
     p.q_slots = p.q_paired ? (n_qt + 1) / 2 : n_qt;
-    p.scale = scale;
-    p.scale_log2 = scale * 1.44269504088896340736f;
-    p.wl = mask.wl;
-    p.wr = mask.wr;
     if (deterministic) return hip_status(fa::launch_bwd(d, mask.mode, false, p, (hipStream_t)stream));
     return hip_status(fa::launch_bwd_atomic(d, mask.mode, false, p, (long)rows, (hipStream_t)stream));
 }

@@ -113,5 +113,8 @@ hipError_t launch_bwd(int d, int mask, bool varlen, BwdParams p, hipStream_t str
 // query rows, one key-side kernel adding dQ into p.dqacc with atomics, and
 // the dQ conversion.
 hipError_t launch_bwd_atomic(int d, int mask, bool varlen, BwdParams p, long rows, hipStream_t stream);
+// fp32 backward (fa_bwd_f32.hip): the dQ kernel (which also writes D and
+// LSE2), then the dK/dV kernel; q_slots and kv_slots count 64-row tiles.
+hipError_t launch_bwd_f32(int d, int mask, BwdParams p, hipStream_t stream);
 
 }  // namespace fa

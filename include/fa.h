@@ -127,8 +127,9 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes and mode: two
  * float32 row vectors [B,H,Nq] (the LSE in base-2 units and D = rowsum(dO *
- * O)) and, unless `deterministic`, a float32 dQ buffer [B,H,Nq,d]; each part
- * rounded up to 256 bytes.  Returns 0 for invalid sizes or dtype.
+ * O)) and, for FA_BF16 unless `deterministic`, a float32 dQ buffer
+ * [B,H,Nq,d]; each part rounded up to 256 bytes.  Returns 0 for invalid sizes
+ * or dtype.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int deterministic);
 
@@ -172,8 +173,12 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, in
  * relative (one more MFMA k-step instead of a subtraction per score), so
  * dQ and dK see D to within that rounding.
  *
- * Only FA_BF16 is accepted (FA_ERR_DTYPE otherwise).  Calls that share a
- * workspace must not overlap.
+ * FA_F32: every product in true float32 (the 32x32x2 fp32 MFMA) with float32
+ * D and LSE; one algorithm, the deterministic one (a query-side kernel for dQ,
+ * a key-side kernel for dK and dV), whatever `deterministic` says, so every
+ * output is bitwise repeatable and the workspace is the two row vectors.
+ *
+ * Calls that share a workspace must not overlap.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dO, void* dq, void* dk, void* dv,

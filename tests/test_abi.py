@@ -95,7 +95,10 @@ def test_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 128, fa.FA_BF16, 7) == 2 * 256
     for det in (0, 1):
         assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 96, fa.FA_BF16, det) == 0
-        assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_F32, det) == 0
+        # fp32 runs the deterministic kernels in either mode: the two row vectors only
+        assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, fa.FA_F32, det) == 2 * 256
+        assert fa.fa_bwd_workspace_bytes(2, 3, 300, 5, 128, fa.FA_F32, det) == 2 * 1800 * 4 + 2 * 224
+        assert fa.fa_bwd_workspace_bytes(1, 1, 3, 5, 64, 7, det) == 0
         assert fa.fa_bwd_workspace_bytes(-1, 1, 3, 5, 64, fa.FA_BF16, det) == 0
         assert fa.fa_bwd_workspace_bytes(1, 1, 0, 5, 64, fa.FA_BF16, det) == 0
 
@@ -110,7 +113,7 @@ def bwd(**kw):
 
 def test_bwd_validation_codes():
     for det in (0, 1):
-        assert bwd(deterministic=det, dtype=fa.FA_F32) == -4
+        assert bwd(deterministic=det, dtype=7) == -4
         assert bwd(deterministic=det, d=32) == -3
         assert bwd(deterministic=det, Nk=-1) == -2
         assert bwd(deterministic=det, scale=0.0) == -8
@@ -125,6 +128,21 @@ def test_bwd_validation_codes():
     # the atomic mode's workspace does not fit a deterministic-sized buffer
     small = fa.fa_bwd_workspace_bytes(1, 2, 32, 32, 64, fa.FA_BF16, 1)
     assert bwd(deterministic=0, workspace_bytes=small) == -6
+    # fp32 takes the same checks (every call here stops before a launch)
+    for det in (0, 1):
+        f32 = dict(deterministic=det, dtype=fa.FA_F32)
+        need = fa.fa_bwd_workspace_bytes(1, 2, 32, 32, 64, fa.FA_F32, det)
+        assert need == small
+        assert bwd(workspace_bytes=need - 1, **f32) == -6
+        assert bwd(workspace=0, **f32) == -6
+        assert bwd(d=96, **f32) == -3
+        assert bwd(dv=0, **f32) == -1
+        assert bwd(q=FAKE_MIS, **f32) == -5
+        assert bwd(scale=float("inf"), **f32) == -8
+        assert bwd(B=0, **f32) == 0
+    # the key-side grid (64-key tiles) must fit in 32 bits, whatever Nq is
+    assert bwd(B=1 << 14, H=1 << 14, Nq=32, Nk=1000) == -2
+    assert bwd(B=1 << 14, H=1 << 14, Nq=32, Nk=1000, dtype=fa.FA_F32) == -2
 
 
 def bwd_noalloc(**kw):
@@ -136,7 +154,7 @@ def bwd_noalloc(**kw):
 
 def test_bwd_noalloc_validation_codes():
     # fa_bwd's own checks, before any HIP call
-    assert bwd_noalloc(dtype=fa.FA_F32) == -4
+    assert bwd_noalloc(dtype=7) == -4
     assert bwd_noalloc(d=32) == -3
     assert bwd_noalloc(Nk=-1) == -2
     assert bwd_noalloc(scale=float("nan")) == -8
@@ -225,7 +243,8 @@ def test_window_validation_codes():
         assert fwdw(window_left=wl, window_right=wr, k=FAKE_MIS) == -5
         assert fwdw(window_left=wl, window_right=wr, scale=0.0) == -8
         assert fwdw(window_left=wl, window_right=wr, B=0, q=0, k=0, v=0, o=0, lse=0) == 0
-        assert bwdw(window_left=wl, window_right=wr, dtype=fa.FA_F32) == -4
+        assert bwdw(window_left=wl, window_right=wr, dtype=7) == -4
+        assert bwdw(window_left=wl, window_right=wr, dtype=fa.FA_F32, workspace=0) == -6
         assert bwdw(window_left=wl, window_right=wr, workspace=0) == -6
         assert bwdw(window_left=wl, window_right=wr, dk=0) == -1
         assert bwdw(window_left=wl, window_right=wr, B=0) == 0
