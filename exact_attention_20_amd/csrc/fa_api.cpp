@@ -76,9 +76,13 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     p.Nq = Nq;
     p.Nk = Nk;
     p.n_qtiles = n_qtiles;
-    p.paired = fa::fwd_pair_tiles(dtype, d, mask.mode == fa::kMaskCausal, BH, n_qtiles) ? 1 : 0;
+    const bool causal = mask.mode == fa::kMaskCausal;
+    const int persist = fa::fwd_persist_grid(dtype, d, causal, BH, n_qtiles);
+    p.paired = (persist > 0 || fa::fwd_pair_tiles(dtype, d, causal, BH, n_qtiles)) ? 1 : 0;
+    p.persist = persist > 0 ? 1 : 0;
     p.n_slots = p.paired ? (n_qtiles + 1) / 2 : n_qtiles;
-    p.total_wg = (int)(BH * p.n_slots);
+    p.total_wg = persist > 0 ? persist : (int)(BH * p.n_slots);
+    p.BH = (int)BH;
     p.scale_log2 = scale * 1.44269504088896340736f;
     p.wl = mask.wl;
     p.wr = mask.wr;

@@ -83,8 +83,20 @@ constexpr int fwd_waves_per_simd() { return D == 64 ? 3 : 2; }
 // VARLEN: the (batch, head) pair's lengths and rows come from the packed
 // variable-length batch in p.vl; n_slots then counts the query tiles of the
 // longest sequence, and a workgroup past its own sequence's tiles exits.
-template <int D, int MASK, bool SPLIT, bool VARLEN = false>
+// PERSIST: a persistent grid (p.total_wg workgroups, a multiple of 8, about
+// as many as fit on the device at once) over mirrored pairs of query tiles
+// (p.paired, an even p.n_qtiles; p.n_slots = n_qtiles / 2 pairs per head).
+// Workgroup w serves the heads h = w (mod 8) -- one XCD's, as the hardware
+// deals workgroup ids to the eight XCDs in turn -- taking their pairs
+// l, l + G, l + 2G, ... (l = w / 8, G = p.total_wg / 8) in head-major order,
+// so each XCD's workgroups share the K/V of a few heads at a time.  Every
+// pair holds the same causal work, so the workgroups stay balanced, and a
+// workgroup prefetches its next item's first key tile even when the item
+// belongs to another head; no workgroup waits to be dispatched after the
+// first.
+template <int D, int MASK, bool SPLIT, bool VARLEN = false, bool PERSIST = false>
 __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(FwdParams p) {
+    static_assert(!PERSIST || (!SPLIT && !VARLEN), "the persistent schedule is for whole fixed-length query tiles");
     constexpr int BR = 128, BC = 64;
     constexpr int NKK = D / 16;        // k-steps over d for S^T
     constexpr int NKB = BC / 32;       // 32-key blocks per tile
@@ -119,6 +131,9 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         split = r % p.n_splits;
     } else if (VARLEN) {
         varlen_slot(p.vl, p.n_slots, blockIdx.x, bh, slot);
+    } else if (PERSIST) {
+        bh = blockIdx.x & 7;   // set per item below
+        slot = 0;
     } else {
         map_head_tile(blockIdx.x, p.total_wg, p.n_slots, bh, slot);
     }
@@ -129,7 +144,15 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     const int Nq = sg.Nq, Nk = sg.Nk, off = Nk - Nq;
     const int nqt = VARLEN ? (Nq + BR - 1) / BR : p.n_qtiles;
     if (VARLEN && slot >= nqt) return;   // past the sequence's last query tile
-    const int n_items = (!SPLIT && p.paired && slot != nqt - 1 - slot) ? 2 : 1;
+    // persistent schedule: this workgroup's XCD share x, its index l there,
+    // G workgroups per share, and its pairs l, l + G, ... of the share's
+    // U = heads_x * n_slots pairs (heads x, x + 8, ...)
+    const int px = blockIdx.x & 7, pl = blockIdx.x >> 3, pG = p.total_wg >> 3;
+    int n_items = (!SPLIT && p.paired && slot != nqt - 1 - slot) ? 2 : 1;
+    if constexpr (PERSIST) {
+        const int U = ((p.BH - px + 7) >> 3) * p.n_slots;
+        n_items = pl < U ? 2 * ((U - pl + pG - 1) / pG) : 0;
+    }
     // right bound: key <= query + offr; left bound (windows): key >= query + offl
     constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
     const int offr = off + (MASK == kMaskWindow ? p.wr : 0);
@@ -140,6 +163,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     const bf16* Qh = (const bf16*)p.q + sg.q_row0 * D;
     const bf16* Kh = (const bf16*)p.k + sg.k_row0 * D;
     const bf16* Vh = (const bf16*)p.v + sg.k_row0 * D;
+    const uint32_t q_bytes = (uint32_t)Nq * D * 2, k_bytes = (uint32_t)Nk * D * 2;
 
     // Buffer resources over this head's Q, K and V: rows past Nq / Nk read as
     // zero, so ragged tails need no branches.
@@ -150,13 +174,17 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // the end-of-tile barrier instead.
     const KCopy kcopier(wave, lane);
     const VCopy vcopier(wave, lane);
-    const i32x4 rk_w = make_rsrc_words(Kh, (uint32_t)Nk * D * 2);
-    const i32x4 rv_w = make_rsrc_words(Vh, (uint32_t)Nk * D * 2);
+    // (set per item under the persistent schedule; nk_w, nv_w, nq_w are the
+    // next item's, which the last key tile and the epilogue prefetch)
+    i32x4 rk_w = make_rsrc_words(Kh, k_bytes);
+    i32x4 rv_w = make_rsrc_words(Vh, k_bytes);
+    i32x4 nk_w = rk_w, nv_w = rv_w;
     const uint32_t smem_lds = lds_address(smem);
-    auto load_tile = [&](int k0, int buf) {
-        kcopier.issue(rk_w, k0, smem_lds + buf * BUF_BYTES);
-        vcopier.issue(rv_w, k0, smem_lds + buf * BUF_BYTES + K_BYTES);
+    auto load_tile_r = [&](const i32x4& rk, const i32x4& rv, int k0, int buf) {
+        kcopier.issue(rk, k0, smem_lds + buf * BUF_BYTES);
+        vcopier.issue(rv, k0, smem_lds + buf * BUF_BYTES + K_BYTES);
     };
+    auto load_tile = [&](int k0, int buf) { load_tile_r(rk_w, rv_w, k0, buf); };
 
     // Q takes the same route: the BR x D query tile (exactly one K + V
     // buffer) is copied into whichever buffer is idle at the start of an
@@ -171,8 +199,10 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     const uint32_t kbase = kLin ? lin_row_base<BC, PK>(lane) : 0u;
     const uint32_t qbase = kLin ? lin_row_base<BR, PK>(lane) : 0u;
     const uint32_t trbase = kLin ? lin_tr_base<PV>(lane) : 0u;
-    const i32x4 rq_w = make_rsrc_words(Qh, (uint32_t)Nq * D * 2);
-    auto load_q = [&](int q0_, int buf) { qcopier.issue(rq_w, q0_, smem_lds + buf * BUF_BYTES); };
+    i32x4 rq_w = make_rsrc_words(Qh, q_bytes);
+    i32x4 nq_w = rq_w;
+    auto load_q_r = [&](const i32x4& rq, int q0_, int buf) { qcopier.issue(rq, q0_, smem_lds + buf * BUF_BYTES); };
+    auto load_q = [&](int q0_, int buf) { load_q_r(rq_w, q0_, buf); };
     bf16x8 qreg[NKK];
     // Key tiles a query tile needs: causal stops after the last key its last
     // query can see; tiles beyond are skipped entirely.
@@ -187,7 +217,38 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     bool prefetched = false;  // its Q and first key tile were issued by the previous item
     bool careful = false;     // recomputation of an item: row maximum on every tile
     for (int it = 0; it < n_items; ++it) {
-    const int qt = it == 0 ? nqt - 1 - slot : slot;
+    // this item's query tile, and the next item's (-1: none)
+    int qt, nxt_qt = -1;
+    if constexpr (PERSIST) {
+        // item it: pair l + (it / 2) G of the share, its tile n-1-s, then s
+        const int u = pl + (it >> 1) * pG, hh = u / p.n_slots, s_ = u - hh * p.n_slots;
+        bh = 8 * hh + px;
+        qt = (it & 1) ? s_ : nqt - 1 - s_;
+        sg.q_row0 = (size_t)bh * Nq;
+        sg.k_row0 = (size_t)bh * Nk;
+        Qh = (const bf16*)p.q + sg.q_row0 * D;
+        rq_w = make_rsrc_words(Qh, q_bytes);
+        rk_w = make_rsrc_words((const bf16*)p.k + sg.k_row0 * D, k_bytes);
+        rv_w = make_rsrc_words((const bf16*)p.v + sg.k_row0 * D, k_bytes);
+        if (it + 1 < n_items) {
+            if (!(it & 1)) {   // the mirror tile of the same head
+                nxt_qt = s_;
+                nq_w = rq_w;
+                nk_w = rk_w;
+                nv_w = rv_w;
+            } else {           // the next pair: another head, probably
+                const int u2 = u + pG, hh2 = u2 / p.n_slots, s2 = u2 - hh2 * p.n_slots;
+                const size_t bh2 = 8 * (size_t)hh2 + px;
+                nxt_qt = nqt - 1 - s2;
+                nq_w = make_rsrc_words((const bf16*)p.q + bh2 * Nq * D, q_bytes);
+                nk_w = make_rsrc_words((const bf16*)p.k + bh2 * Nk * D, k_bytes);
+                nv_w = make_rsrc_words((const bf16*)p.v + bh2 * Nk * D, k_bytes);
+            }
+        }
+    } else {
+        qt = it == 0 ? nqt - 1 - slot : slot;
+        if (it + 1 < n_items) nxt_qt = slot;
+    }
     const int q0 = qt * BR;
     const int qw = q0 + wave * 32;     // this wave's first query
     const int qi = qw + l32;           // this lane's query
@@ -198,8 +259,8 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // last key + 1 this wave sees; a wave whose rows all lie past Nq skips the math
     const int kend_w = qw >= Nq ? 0 : kRight ? min(Nk, qw + 32 + offr) : Nk;
     const int kbeg_w = kLeft ? qw + offl : 0;   // first key the wave's first row sees
-    const bool more = it + 1 < n_items;
-    const int next_ntiles = more ? tiles_of(slot) - first_tile_of(slot) : 0;
+    const bool more = nxt_qt >= 0;
+    const int next_ntiles = more ? tiles_of(nxt_qt) - first_tile_of(nxt_qt) : 0;
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -235,7 +296,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         // the other buffer takes the next key tile, or the next item's first
         const bool has_next = t + 1 < t_hi || next_ntiles > 0;
         if (t + 1 < t_hi) load_tile(k0 + BC, buf ^ 1);
-        else if (has_next) load_tile(first_tile_of(slot) * BC, buf ^ 1);
+        else if (has_next) load_tile_r(nk_w, nv_w, first_tile_of(nxt_qt) * BC, buf ^ 1);
 
         if (k0 < kend_w && (!kLeft || k0 + BC > kbeg_w)) {
             // ---- S^T = K Q^T (fp32 accumulators) ----
@@ -406,7 +467,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     prefetched = next_ntiles > 0 && ntiles > 0;
     b0 = (b0 + ntiles) & 1;
     constexpr bool kStageO = D == 128 || MASK != kMaskCausal;
-    if (!kStageO && prefetched) load_q(slot * BR, b0 ^ 1);
+    if (!kStageO && prefetched) load_q_r(nq_w, nxt_qt * BR, b0 ^ 1);
 
     // ---- epilogue: O = O~ / l, LSE = ln2 * (m + log2 l) ----
     const float l_tot = xhalf_sum(l_run);
@@ -500,7 +561,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         // every wave has read its staged rows before the buffer takes the
         // next item's Q tile (or, unprefetched, that item's own copies)
         tile_barrier();
-        if (prefetched) load_q(slot * BR, b0 ^ 1);
+        if (prefetched) load_q_r(nq_w, nxt_qt * BR, b0 ^ 1);
     }
     }   // items
 }
@@ -738,11 +799,23 @@ int fwd_rows_per_workgroup(int dtype, int d) {
 // 256 CUs x 2 resident workgroups = 512 slots; pair when the unpaired grid
 // covers them at least four times and a workgroup's start-up (Q and first key
 // tile from HBM) and epilogue are a noticeable share of its work: short
-// sequences with d = 64 (measured +10% at N=4096).  At d = 128 pairing gained
-// nothing at N=4096 and cost L2 locality (twice the heads in flight per XCD:
-// 1.4x the L2 miss traffic), and at N=32768 it lost 1.6%.
+// sequences with d = 64 (measured +10% at N=4096).  At d = 128 pairing on its
+// own gained nothing at N=4096 and cost L2 locality (twice the heads in flight
+// per XCD: 1.4x the L2 miss traffic), and at N=32768 it lost 1.6%; there the
+// pairs run on the persistent grid below (+1% to +1.6% at N = 4096: no
+// workgroup waits for dispatch after the first).
 bool fwd_pair_tiles(int dtype, int d, bool causal, long bh, int n_qtiles) {
     return dtype == 1 && d == 64 && causal && n_qtiles >= 2 && n_qtiles <= 64 && bh * n_qtiles >= 4 * 512;
+}
+
+// The persistent causal d = 128 grid: one workgroup per resident slot (512),
+// when the heads' mirrored pairs of query tiles give every workgroup at
+// least two of them.
+int fwd_persist_grid(int dtype, int d, bool causal, long bh, int n_qtiles) {
+    constexpr int kSlots = 512;
+    const bool ok = dtype == 1 && d == 128 && causal && n_qtiles >= 2 && n_qtiles % 2 == 0 &&
+                    bh * (n_qtiles / 2) >= 2L * kSlots;
+    return ok ? kSlots : 0;
 }
 
 template <typename KernelT>
@@ -755,6 +828,8 @@ static hipError_t launch(KernelT kernel, int grid, int block, const FwdParams& p
 template <int MASK>
 static hipError_t launch_fwd_mask(int dtype, int d, const FwdParams& p, hipStream_t stream) {
     const int grid = p.total_wg;
+    if constexpr (MASK == kMaskCausal)
+        if (p.persist) return launch(fwd_bf16_kernel<128, kMaskCausal, false, false, true>, grid, 256, p, stream);
     if (dtype == 1)
         return d == 64 ? launch(fwd_bf16_kernel<64, MASK, false>, grid, 256, p, stream)
                        : launch(fwd_bf16_kernel<128, MASK, false>, grid, 256, p, stream);

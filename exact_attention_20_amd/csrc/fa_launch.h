@@ -47,11 +47,12 @@ struct FwdParams {
     int n_qtiles;      // ceil(Nq / BR) for the chosen kernel
     int n_slots;       // workgroups per (batch, head): n_qtiles, or ceil(n_qtiles / 2) when paired
     int paired;        // bf16 kernel: a workgroup runs query tiles n-1-j and j of one head
-    int total_wg;      // B * H * n_slots (split-KV: B * H * n_qtiles * n_splits)
+    int persist;       // bf16 causal d = 128: the persistent grid over the pairs (paired = 1)
+    int total_wg;      // B * H * n_slots (split-KV: B * H * n_qtiles * n_splits; persistent: the grid)
     float scale_log2;  // scale * log2(e)
     int wl, wr;        // window reaches (kMaskWindow only)
+    int BH;               // B * H (split-KV and persistent modes)
     // split-KV mode only
-    int BH;
     int n_splits;         // runs of key tiles per query tile
     int tiles_per_split;  // 64-key tiles per run
     float* o_part;        // [n_splits, B*H, Nq, d] fp32 partial outputs
@@ -92,6 +93,9 @@ int fwd_rows_per_workgroup(int dtype, int d);
 // causal only, where it evens out the work, and only for grids large enough
 // that halving the workgroup count still fills the GPU several times over.
 bool fwd_pair_tiles(int dtype, int d, bool causal, long bh, int n_qtiles);
+// The persistent grid size for a forward call, or 0 for the one-workgroup-
+// per-item launch.
+int fwd_persist_grid(int dtype, int d, bool causal, long bh, int n_qtiles);
 // The same decision for the backward kernels' key and query tiles.
 bool bwd_pair_tiles(bool causal, long bh, int n_tiles);
 

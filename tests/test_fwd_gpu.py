@@ -154,6 +154,44 @@ def test_paired_query_tiles_sampled_heads(case):
         check_forward(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, "bf16", f"{case} head {bh}")
 
 
+# ------------------------------------- persistent grid (causal d = 128, large)
+# With causal masking, d = 128, an even query-tile count and at least 1024
+# mirrored pairs of 128-row query tiles, the forward runs 512 persistent
+# workgroups, each taking pairs of the heads of one XCD share (heads = w mod 8)
+# and prefetching its next item across heads.  These shapes take that path
+# with a ragged tail and a head count that leaves the shares unequal, and with
+# Nq != Nk both ways; every sampled head must also equal, bitwise, the same
+# head run alone (one workgroup per query tile), since only the schedule
+# differs.
+PERSIST = [
+    # B, H, Nq, Nk
+    (1, 150, 1700, 1700),     # 14 query tiles, 36-row tail; 150 heads: shares of 19 and 18
+    (4, 64, 1024, 1500),      # Nk > Nq (bottom-right causal alignment)
+    (4, 64, 1280, 700),       # Nq > Nk: the first 580 rows see no key
+]
+
+
+@pytest.mark.parametrize("case", PERSIST, ids=lambda c: "-".join(map(str, c)))
+def test_persistent_grid_sampled_heads_and_bitwise(case):
+    B, H, Nq, Nk = case
+    d = 128
+    n_qt = (Nq + 127) // 128
+    assert n_qt % 2 == 0 and B * H * (n_qt // 2) >= 1024   # the persistent path
+    banner(f"fwd persistent {case}")
+    q, k, v = wl.make_inputs(B, H, Nq, Nk, d, "bf16", seed=950 + Nq + Nk)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = gpu_fwd(q, k, v, scale, True)
+    g = torch.Generator().manual_seed(Nq * 5 + Nk)
+    heads = [0, 1, 7, B * H - 1] + torch.randperm(B * H, generator=g)[:3].tolist()
+    for bh in heads:
+        b, h = divmod(bh, H)
+        o_ref, lse_ref = attention_forward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), scale, True)
+        check_forward(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, "bf16", f"{case} head {bh}")
+        o1, lse1 = gpu_fwd(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], scale, True)
+        assert torch.equal(o1[0, 0].cpu(), o[b, h].cpu()), f"{case} head {bh}: O differs from the lone head"
+        assert torch.equal(lse1[0, 0].cpu(), lse[b, h].cpu()), f"{case} head {bh}: LSE differs"
+
+
 # ------------------------------------------------------------------ page pins
 def _pad_fp32(x, width):
     out = torch.zeros(x.shape[0], width, dtype=torch.float32)
