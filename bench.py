@@ -334,6 +334,36 @@ def valu_probe(sclk_ghz: float, repeats: int = 5) -> dict:
     return res
 
 
+def soft_exp2_ab(fa, w, argv, stream, steps: int, rounds: int) -> dict:
+    """fa_fwd (period 0) against fa_fwd_soft_exp2 with periods 8, 4 and 2 on
+    one workload: after the hardware ceilings (which settle the clock) and a
+    warm-up of each, ``rounds`` rounds that time ``steps`` launches of every
+    variant in turn; the median over rounds of each variant's ms per launch.
+    (Its parity is the GPU tests'.)"""
+    fns = {}
+    for period in (0, 8, 4, 2):
+        if period == 0:
+            fns[period] = lambda: fa.fa_fwd(*argv)
+        else:
+            fns[period] = (lambda per: lambda: fa.fa_fwd_soft_exp2(*argv[:13], per, argv[13]))(period)
+    gemm_ceiling()
+    mfma_probe()
+    res = {p_: [] for p_ in fns}
+    for p_, fn in fns.items():
+        time_launches(fn, stream, 3, 3)
+    for _ in range(rounds):
+        for p_, fn in fns.items():
+            res[p_].append(time_launches(fn, stream, steps, 1))
+    med = {p_: sorted(v)[len(v) // 2] for p_, v in res.items()}
+    flops = fwd_flops(w)
+    return {"soft_exp2_ab": {"workload": w.name, "rounds": rounds, "steps": steps,
+                             "median_ms": {str(p_): round(m, 5) for p_, m in med.items()},
+                             "tflops": {str(p_): round(flops / (m * 1e-3) / 1e12, 1) for p_, m in med.items()},
+                             "vs_hardware_exp": {str(p_): round(med[0] / m - 1.0, 4) for p_, m in med.items() if p_},
+                             "note": "period 0 = fa_fwd (v_exp_f32 throughout); period p = one exponential "
+                                     "in p by the degree-3 polynomial on the FMA pipe"}}
+
+
 def time_launches(fn, stream, steps: int, warmup: int) -> float:
     """Average ms per call of ``fn`` with HIP events on ``stream``."""
     import torch
@@ -658,6 +688,10 @@ def main():
     ap.add_argument("--summarize-sq", nargs="+", metavar="PMC_DIR",
                     help="print per-kernel means of the counters in rocprofv3 --pmc output "
                          "directories as a markdown table (no GPU needed)")
+    ap.add_argument("--soft-exp2-ab", type=int, default=0, metavar="ROUNDS",
+                    help="instead of the benchmark line, time fa_fwd against fa_fwd_soft_exp2 "
+                         "(one exponential in 8, 4, 2 by the FMA-pipe polynomial) on --workload "
+                         "in ROUNDS interleaved rounds of --steps launches; one JSON line")
     ap.add_argument("--sclk-ghz", type=float, default=2.1,
                     help="core clock for --summarize-sq's MFMA busy share")
     args = ap.parse_args()
@@ -744,6 +778,10 @@ def main():
             st = fa.fa_fwd_splitkv(*sargv)
             if st != 0:
                 raise fa.FAError(st, "fa_fwd_splitkv")
+
+    if args.soft_exp2_ab:
+        print(json.dumps(soft_exp2_ab(fa, w, argv, stream, args.steps, args.soft_exp2_ab)), flush=True)
+        return
 
     # Parity first (the cpu_baseline leg): one launch, its output against the
     # fp64 oracle on every head the bounded CPU sample reaches.

@@ -93,6 +93,8 @@ def load_library() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_soft_exp2.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_fwd_soft_exp2.restype = i
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
@@ -128,6 +130,11 @@ def _p(x):
 def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, stream) -> int:
     return load_library().fa_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Nq, Nk, d,
                                  float(scale), int(causal), int(dtype), _p(stream))
+
+
+def fa_fwd_soft_exp2(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, period, stream) -> int:
+    return load_library().fa_fwd_soft_exp2(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Nq, Nk, d,
+                                           float(scale), int(causal), int(dtype), int(period), _p(stream))
 
 
 def fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, n_splits,
@@ -258,9 +265,11 @@ def _window_args(causal, window):
 
 
 def attention_forward(q, k, v, scale=None, causal=False, out=None, lse=None, want_lse=True,
-                      window=None):
+                      window=None, soft_exp2=0):
     """O = softmax(scale * q k^T) v and the natural-log LSE, via fa_fwd (or
-    fa_fwd_window when a local ``window`` is given).
+    fa_fwd_window when a local ``window`` is given, or fa_fwd_soft_exp2 when
+    ``soft_exp2`` is 2, 4 or 8: one exponential in that many by a polynomial
+    on the FMA pipe; bf16, no window).
 
     q [B,H,Nq,d], k and v [B,H,Nk,d]; bf16 or fp32; contiguous; on the GPU.
     Returns (o, lse); lse is None when want_lse is False and none is given.
@@ -282,15 +291,22 @@ def attention_forward(q, k, v, scale=None, causal=False, out=None, lse=None, wan
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     w = _window_args(causal, window)
     lse_p = lse.data_ptr() if lse is not None else 0
+    if soft_exp2 and w is not None:
+        raise ValueError("soft_exp2 takes the causal or unmasked forward, not a window")
+    name = "fa_fwd_window" if w is not None else "fa_fwd_soft_exp2" if soft_exp2 else "fa_fwd"
     with torch.cuda.device(q.device):
-        if w is None:
-            st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
-                        B, H, Nq, Nk, d, scale, causal, _dtype_code(q), _stream(q.device))
-        else:
+        if w is not None:
             st = fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
                                B, H, Nq, Nk, d, scale, w[0], w[1], _dtype_code(q), _stream(q.device))
+        elif soft_exp2:
+            st = fa_fwd_soft_exp2(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
+                                  B, H, Nq, Nk, d, scale, causal, _dtype_code(q), soft_exp2,
+                                  _stream(q.device))
+        else:
+            st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
+                        B, H, Nq, Nk, d, scale, causal, _dtype_code(q), _stream(q.device))
     if st != 0:
-        raise FAError(st, "fa_fwd" if w is None else "fa_fwd_window")
+        raise FAError(st, name)
     return out, lse
 
 

@@ -56,7 +56,7 @@ int window_mask(int window_left, int window_right, Mask* m) {
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Nq, int Nk, int d, float scale, Mask mask,
-             int dtype, void* stream) {
+             int dtype, void* stream, int soft_exp2 = 0) {
     int st = check_common(B, H, Nq, Nk, d, scale, dtype);
     if (st != FA_OK) return st;
     const long BH = (long)B * H;
@@ -83,6 +83,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     p.n_slots = p.paired ? (n_qtiles + 1) / 2 : n_qtiles;
     p.total_wg = persist > 0 ? persist : (int)(BH * p.n_slots);
     p.BH = (int)BH;
+    p.soft_exp2 = soft_exp2;
     p.scale_log2 = scale * 1.44269504088896340736f;
     p.wl = mask.wl;
     p.wr = mask.wr;
@@ -281,6 +282,16 @@ extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* 
     return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, d, scale, m, dtype, stream);
 }
 
+extern "C" int fa_fwd_soft_exp2(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                                int dtype, int period, void* stream) {
+    const int st = check_common(B, H, Nq, Nk, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (period != 2 && period != 4 && period != 8) return FA_ERR_PERIOD;
+    return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal_mask(causal), dtype, stream, period);
+}
+
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dO, void* dq, void* dk, void* dv,
                       int B, int H, int Nq, int Nk, int d, float scale, int causal,
@@ -448,6 +459,7 @@ extern "C" const char* fa_strerror(int status) {
         case FA_ERR_SCALE: return "scale must be finite and > 0";
         case FA_ERR_WINDOW: return "window reaches must be >= 0, or -1 for an unbounded side";
         case FA_ERR_SCRATCH: return "the call needs more than fa_bwd_noalloc's static buffer (FA_NOALLOC_SCRATCH_BYTES)";
+        case FA_ERR_PERIOD: return "the software-exponential period must be 2, 4 or 8";
         default: return "unknown status";
     }
 }

@@ -49,6 +49,24 @@ __device__ __forceinline__ f32x16 zero16() {
 // 2^x on the hardware transcendental unit (v_exp_f32): -inf -> 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x on the FMA pipe instead of the transcendental unit ("FlashAttention
+// 1～4 全解汇总", FlashAttention-4, software-emulated exponential): x = n + f
+// with n = floor(x) and f in [0, 1); 2^f by a degree-3 polynomial in Horner
+// form whose coefficients minimise the maximum relative error on [0, 1] (a
+// Remez exchange fit, exp2_poly.py beside this package: |p(f) / 2^f - 1| <=
+// 7.5e-5, far below bf16's 2^-9 rounding of P); 2^n goes into the exponent
+// with ldexp.  x is first raised to -200 (NaN kept), so -inf -- a masked
+// score -- and anything below -150 give exactly 0.
+__device__ __forceinline__ float exp2_poly(float x) {
+    x = x < -200.f ? -200.f : x;
+    const float n = floorf(x);
+    const float f = x - n;
+    float p = fmaf(0x1.3f96a4p-4f, f, 0x1.cefc4cp-3f);
+    p = fmaf(p, f, 0x1.64444cp-1f);
+    p = fmaf(p, f, 0x1.fff632p-1f);
+    return ldexpf(p, (int)n);
+}
+
 // Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -94,8 +94,12 @@ constexpr int fwd_waves_per_simd() { return D == 64 ? 3 : 2; }
 // workgroup prefetches its next item's first key tile even when the item
 // belongs to another head; no workgroup waits to be dispatched after the
 // first.
-template <int D, int MASK, bool SPLIT, bool VARLEN = false, bool PERSIST = false>
+// SWEXP: 0, or 2, 4 or 8 for the opt-in software exponential (f3): one
+// exponential of P in SWEXP is computed by exp2_poly on the FMA pipe instead
+// of v_exp_f32 (chosen at compile time by its position in the tile).
+template <int D, int MASK, bool SPLIT, bool VARLEN = false, bool PERSIST = false, int SWEXP = 0>
 __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(FwdParams p) {
+    static_assert(SWEXP == 0 || SWEXP == 2 || SWEXP == 4 || SWEXP == 8, "one exponential in 2, 4 or 8");
     static_assert(!PERSIST || (!SPLIT && !VARLEN), "the persistent schedule is for whole fixed-length query tiles");
     constexpr int BR = 128, BC = 64;
     constexpr int NKK = D / 16;        // k-steps over d for S^T
@@ -392,7 +396,10 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float p0 = exp2_hw(fmaf(s[kb][i0 + 2 * j], p.scale_log2, nbase));
-                    const float p1 = exp2_hw(fmaf(s[kb][i0 + 2 * j + 1], p.scale_log2, nbase));
+                    const float x1 = fmaf(s[kb][i0 + 2 * j + 1], p.scale_log2, nbase);
+                    // the tile's exponential number kc*8 + 2j + 1 of 32
+                    const bool soft = SWEXP > 0 && (kc * 8 + 2 * j + 1) % (SWEXP > 0 ? SWEXP : 1) == SWEXP - 1;
+                    const float p1 = soft ? exp2_poly(x1) : exp2_hw(x1);
                     if (kc == 0 && j < 2) {
                         rs[2 * j] = p0;
                         rs[2 * j + 1] = p1;
@@ -418,13 +425,15 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
             // training-step forward, -1.3% at N = 32768.
             {
                 constexpr int vAhead = 2;
-                __builtin_amdgcn_sched_group_barrier(0x002, 24, 1);
+                // software exponentials add 8 VALU instructions each, 8 / SWEXP per block
+                constexpr int kExtraV = SWEXP > 0 ? 8 * (8 / (SWEXP > 0 ? SWEXP : 1)) : 0;
+                __builtin_amdgcn_sched_group_barrier(0x002, 24 + kExtraV, 1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * vAhead, 1);
 #pragma unroll
                 for (int i = 0; i < NKC * NDB; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
                     if (i < NKC * NDB - vAhead) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-                    if (i < (NKC - 1) * NDB) __builtin_amdgcn_sched_group_barrier(0x002, 7 * 4 / NDB, 1);
+                    if (i < (NKC - 1) * NDB) __builtin_amdgcn_sched_group_barrier(0x002, (7 * 4 + kExtraV) / NDB, 1);
                 }
             }
         }
@@ -825,9 +834,25 @@ static hipError_t launch(KernelT kernel, int grid, int block, const FwdParams& p
     return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(block), args, 0, s);
 }
 
+// the software-exponential forward (bf16, no window): period p.soft_exp2
+template <int D, int MASK, bool PERSIST>
+static hipError_t launch_soft_exp2(const FwdParams& p, hipStream_t s) {
+    if (p.soft_exp2 == 2) return launch(fwd_bf16_kernel<D, MASK, false, false, PERSIST, 2>, p.total_wg, 256, p, s);
+    if (p.soft_exp2 == 4) return launch(fwd_bf16_kernel<D, MASK, false, false, PERSIST, 4>, p.total_wg, 256, p, s);
+    return launch(fwd_bf16_kernel<D, MASK, false, false, PERSIST, 8>, p.total_wg, 256, p, s);
+}
+
 template <int MASK>
 static hipError_t launch_fwd_mask(int dtype, int d, const FwdParams& p, hipStream_t stream) {
     const int grid = p.total_wg;
+    if constexpr (MASK != kMaskWindow) {
+        if (p.soft_exp2 && dtype == 1) {
+            if (d == 64) return launch_soft_exp2<64, MASK, false>(p, stream);
+            if constexpr (MASK == kMaskCausal)
+                if (p.persist) return launch_soft_exp2<128, MASK, true>(p, stream);
+            return launch_soft_exp2<128, MASK, false>(p, stream);
+        }
+    }
     if constexpr (MASK == kMaskCausal)
         if (p.persist) return launch(fwd_bf16_kernel<128, kMaskCausal, false, false, true>, grid, 256, p, stream);
     if (dtype == 1)

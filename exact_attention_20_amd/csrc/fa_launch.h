@@ -48,6 +48,7 @@ struct FwdParams {
     int n_slots;       // workgroups per (batch, head): n_qtiles, or ceil(n_qtiles / 2) when paired
     int paired;        // bf16 kernel: a workgroup runs query tiles n-1-j and j of one head
     int persist;       // bf16 causal d = 128: the persistent grid over the pairs (paired = 1)
+    int soft_exp2;     // bf16, no window: one exponential in soft_exp2 (2, 4, 8) by exp2_poly; 0 = none
     int total_wg;      // B * H * n_slots (split-KV: B * H * n_qtiles * n_splits; persistent: the grid)
     float scale_log2;  // scale * log2(e)
     int wl, wr;        // window reaches (kMaskWindow only)

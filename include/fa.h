@@ -72,7 +72,8 @@ typedef enum {
     FA_ERR_LAUNCH = -7,     /* the HIP runtime refused a kernel launch       */
     FA_ERR_SCALE = -8,      /* scale is not finite or not > 0                */
     FA_ERR_WINDOW = -9,     /* a window reach below -1                       */
-    FA_ERR_SCRATCH = -10    /* beyond fa_bwd_noalloc's static buffer         */
+    FA_ERR_SCRATCH = -10,   /* beyond fa_bwd_noalloc's static buffer         */
+    FA_ERR_PERIOD = -11     /* fa_fwd_soft_exp2's period is not 2, 4 or 8    */
 } fa_status_t;
 
 /* Largest Nq or Nk accepted (keeps every in-head byte offset within 32 bits). */
@@ -91,6 +92,27 @@ typedef enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Nq, int Nk, int d, float scale, int causal,
            int dtype, void* stream);
+
+/*
+ * fa_fwd with part of the softmax's exponentials computed in software on the
+ * FMA pipe ("FlashAttention 1～4 全解汇总", FlashAttention-4, software-
+ * emulated exponential; the exponent in base 2 as in "01 · IO-awareness、
+ * online softmax 与 tiling" §4): one of every `period` (2, 4 or 8)
+ * exponentials of P is 2^floor(x) * p(x - floor(x)) with p a degree-3
+ * polynomial (Remez minimax fit, relative error <= 7.5e-5), the rest are the
+ * hardware's v_exp_f32.  Arguments, layouts and errors are those of fa_fwd;
+ * bf16 only (FA_ERR_DTYPE otherwise); a period other than 2, 4 or 8 returns
+ * FA_ERR_PERIOD.  Results meet fa_fwd's tolerance but differ from it in the
+ * last bits.
+ *
+ * On MI355X this is slower than fa_fwd: v_exp_f32 issues on the same pipe
+ * as the FMAs (about 2 FMA slots per exponential), while the polynomial takes
+ * 9 VALU instructions, so moving exponentials to it adds VALU work instead of
+ * relieving a separate unit.  It is kept for that measurement.
+ */
+int fa_fwd_soft_exp2(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                     int dtype, int period, void* stream);
 
 /*
  * Split-KV forward ("01 · IO-awareness、online softmax 与 tiling" §2: the

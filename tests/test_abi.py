@@ -35,7 +35,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
-    assert set(syms) == {"fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
+    assert set(syms) == {"fa_fwd", "fa_fwd_soft_exp2", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
                          "fa_bwd_workspace_bytes", "fa_bwd_noalloc", "fa_fwd_window", "fa_bwd_window",
                          "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes",
                          "fa_strerror"}
@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_codes():
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         msg = fa.fa_strerror(code)
         assert msg and msg != "unknown status", code
     assert fa.fa_strerror(-99) == "unknown status"
@@ -345,3 +345,25 @@ def test_resource_usage_remark_parser():
     assert rows[1]["VGPRs Spill"] == "4" and "AGPRs" not in rows[1]
     table = build.resource_table([("a.hip", "void fa::k<64, 1>(fa::FwdParams)", rows[0])])
     assert "| a.hip | `k<64, 1>` | 128 | 0 | 0 |" in table
+
+
+def fwd_soft(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=16, Nk=16, d=64,
+             scale=0.125, causal=0, dtype=fa.FA_BF16, period=4, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_soft_exp2(**a)
+
+
+def test_soft_exp2_validation_codes():
+    # every call here stops before a launch
+    for period in (0, 1, 3, 5, 16, -2):
+        assert fwd_soft(period=period) == -11
+    assert fwd_soft(dtype=fa.FA_F32) == -4
+    assert fwd_soft(dtype=7) == -4
+    assert fwd_soft(d=96) == -3
+    assert fwd_soft(Nq=-1) == -2
+    assert fwd_soft(scale=0.0) == -8
+    assert fwd_soft(q=0) == -1
+    assert fwd_soft(k=FAKE_MIS) == -5
+    assert fwd_soft(B=0, q=0, k=0, v=0, o=0, lse=0) == 0
+    assert "2, 4 or 8" in fa.fa_strerror(-11)
