@@ -129,6 +129,31 @@ def test_planted_jump_in_paired_workgroups():
     check_heads(q, k, v, o, lse, scale, True, heads + [(0, 0)], f"paired A={A}")
 
 
+def test_planted_jump_in_persistent_grid():
+    """d = 128 causal over >= 1024 mirrored pairs of query tiles: the forward
+    runs its persistent grid, where a workgroup's next item may belong to
+    another head and has its first key tile prefetched during the current
+    item's last one.  A recomputation must leave the next items (the mirror
+    tile, and the next head of the same XCD share, h + 8) correct."""
+    B, H, N, d = 1, 64, 4096, 128
+    assert (N // 128) % 2 == 0 and B * H * (N // 256) >= 1024
+    banner(f"fwd planted jump persistent B{B} H{H} N{N} d{d}")
+    q, k, v = wl.make_inputs(B, H, N, N, d, "bf16", seed=4551)
+    heads = [(0, 3), (0, 12), (0, 21), (0, 46)]   # shares 3, 4, 5, 6
+    rows = []
+    for i, (b, h) in enumerate(heads):
+        rows.append((b, h, N - 1 - 41 * i))        # the last query tile: the first item of its pair
+        rows.append((b, h, 300 + 517 * i))         # a light tile: the second item of a pair
+    A = plant(q, k, rows, 200, d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_forward(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all(), "non-finite output"
+    after = [(0, h + 8) for (_, h) in heads if h + 8 < H]
+    check_heads(q, k, v, o, lse, scale, True, heads + after + [(0, 0)], f"persistent A={A}")
+
+
 def test_planted_jump_under_local_window():
     B, H, N, d = 1, 2, 900, 128
     window = (300, 0)
