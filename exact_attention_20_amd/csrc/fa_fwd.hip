@@ -265,6 +265,16 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     const int kbeg_w = kLeft ? qw + offl : 0;   // first key the wave's first row sees
     const bool more = nxt_qt >= 0;
     const int next_ntiles = more ? tiles_of(nxt_qt) - first_tile_of(nxt_qt) : 0;
+    // Under the persistent schedule the second item of a pair walks its key
+    // tiles downwards, from the diagonal: the 16 or so workgroups on a head
+    // start their second items at staggered times, and walking down they all
+    // read the same key tile at the same time (item s of length 2s + 2 begins
+    // when the first, of length 64 - 2s, ends), so the head's K/V stays in
+    // L2 instead of being read at as many offsets as there are workgroups.
+    // The online softmax does not depend on the order of the tiles.
+    const bool rev = PERSIST && (it & 1);
+    const int t_first = rev ? t_hi - 1 : t_lo;   // the item's first key tile
+    const int nxt_first = !more ? 0 : (PERSIST && !(it & 1)) ? tiles_of(nxt_qt) - 1 : first_tile_of(nxt_qt);
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -278,7 +288,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // when that item prefetched this one's first key tile into b0)
     if (!prefetched) {
         load_q(q0, b0 ^ 1);
-        if (ntiles > 0) load_tile(t_lo * BC, b0);
+        if (ntiles > 0) load_tile(t_first * BC, b0);
     }
     vmem_wait_all();
     tile_barrier();
@@ -290,17 +300,18 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     }
     tile_barrier();   // every wave holds its Q rows before b0^1 takes the next key tile
 
-    for (int t = t_lo; t < t_hi; ++t) {
+    for (int i_t = 0; i_t < ntiles; ++i_t) {
+        const int t = rev ? t_first - i_t : t_lo + i_t;
         const int k0 = t * BC;
-        const int buf = (b0 + t - t_lo) & 1;
+        const int buf = (b0 + i_t) & 1;
         const char* kbuf = smem + buf * BUF_BYTES;
         const char* vbuf = kbuf + K_BYTES;
         const char* kread = kbuf + kbase;    // d = 128 tiles: operand = base + immediate
         const char* vread = vbuf + trbase;
         // the other buffer takes the next key tile, or the next item's first
-        const bool has_next = t + 1 < t_hi || next_ntiles > 0;
-        if (t + 1 < t_hi) load_tile(k0 + BC, buf ^ 1);
-        else if (has_next) load_tile_r(nk_w, nv_w, first_tile_of(nxt_qt) * BC, buf ^ 1);
+        const bool has_next = i_t + 1 < ntiles || next_ntiles > 0;
+        if (i_t + 1 < ntiles) load_tile(rev ? k0 - BC : k0 + BC, buf ^ 1);
+        else if (has_next) load_tile_r(nk_w, nv_w, nxt_first * BC, buf ^ 1);
 
         if (k0 < kend_w && (!kLeft || k0 + BC > kbeg_w)) {
             // ---- S^T = K Q^T (fp32 accumulators) ----

@@ -160,9 +160,11 @@ def test_paired_query_tiles_sampled_heads(case):
 # workgroups, each taking pairs of the heads of one XCD share (heads = w mod 8)
 # and prefetching its next item across heads.  These shapes take that path
 # with a ragged tail and a head count that leaves the shares unequal, and with
-# Nq != Nk both ways; every sampled head must also equal, bitwise, the same
-# head run alone (one workgroup per query tile), since only the schedule
-# differs.
+# Nq != Nk both ways.  Each sampled head is also run alone (one workgroup per
+# query tile, every key walk upwards): the query tiles of the upper half, the
+# first item of each pair, walk their keys upwards there too and must be
+# bitwise equal; the lower half walk theirs downwards under the persistent
+# schedule, so they agree to within rounding (the same sums in another order).
 PERSIST = [
     # B, H, Nq, Nk
     (1, 150, 1700, 1700),     # 14 query tiles, 36-row tail; 150 heads: shares of 19 and 18
@@ -188,8 +190,14 @@ def test_persistent_grid_sampled_heads_and_bitwise(case):
         o_ref, lse_ref = attention_forward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), scale, True)
         check_forward(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, "bf16", f"{case} head {bh}")
         o1, lse1 = gpu_fwd(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], scale, True)
-        assert torch.equal(o1[0, 0].cpu(), o[b, h].cpu()), f"{case} head {bh}: O differs from the lone head"
-        assert torch.equal(lse1[0, 0].cpu(), lse[b, h].cpu()), f"{case} head {bh}: LSE differs"
+        o1, lse1, oh, lseh = o1[0, 0].cpu(), lse1[0, 0].cpu(), o[b, h].cpu(), lse[b, h].cpu()
+        up = (n_qt // 2) * 128   # first row of the upper half's query tiles
+        assert torch.equal(o1[up:], oh[up:]), f"{case} head {bh}: O (upper tiles) differs from the lone head"
+        assert torch.equal(lse1[up:], lseh[up:]), f"{case} head {bh}: LSE (upper tiles) differs"
+        fin = torch.isfinite(lse1[:up])
+        assert torch.equal(fin, torch.isfinite(lseh[:up])), f"{case} head {bh}: empty rows differ"
+        assert (lse1[:up][fin] - lseh[:up][fin]).abs().max().item() <= 1e-5 if fin.any() else True
+        assert (o1[:up].float() - oh[:up].float()).abs().max().item() <= 2e-2
 
 
 # ------------------------------------------------------------------ page pins
