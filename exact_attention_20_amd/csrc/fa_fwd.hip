@@ -86,14 +86,15 @@ constexpr int fwd_waves_per_simd() { return D == 64 ? 3 : 2; }
 // PERSIST: a persistent grid (p.total_wg workgroups, a multiple of 8, about
 // as many as fit on the device at once) over mirrored pairs of query tiles
 // (p.paired, an even p.n_qtiles; p.n_slots = n_qtiles / 2 pairs per head).
-// Workgroup w serves the heads h = w (mod 8) -- one XCD's, as the hardware
-// deals workgroup ids to the eight XCDs in turn -- taking their pairs
-// l, l + G, l + 2G, ... (l = w / 8, G = p.total_wg / 8) in head-major order,
-// so each XCD's workgroups share the K/V of a few heads at a time.  Every
-// pair holds the same causal work, so the workgroups stay balanced, and a
-// workgroup prefetches its next item's first key tile even when the item
-// belongs to another head; no workgroup waits to be dispatched after the
-// first.
+// The T = BH * n_slots pairs, in head-major order, are cut into eight equal
+// runs, one per XCD: workgroup w is on XCD x = w mod 8 (the hardware deals
+// workgroup ids to the eight XCDs in turn) and takes pairs l, l + G, l + 2G,
+// ... of run x (l = w / 8, G = p.total_wg / 8), so each XCD's workgroups
+// share the K/V of a few consecutive heads at a time, and every XCD gets the
+// same number of pairs whatever the head count.  Every pair holds the same
+// causal work, so the workgroups stay balanced, and a workgroup prefetches
+// its next item's first key tile even when the item belongs to another head;
+// no workgroup waits to be dispatched after the first.
 // SWEXP: 0, or 2, 4 or 8 for the opt-in software exponential (f3): one
 // exponential of P in SWEXP is computed by exp2_poly on the FMA pipe instead
 // of v_exp_f32 (chosen at compile time by its position in the tile).
@@ -136,7 +137,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     } else if (VARLEN) {
         varlen_slot(p.vl, p.n_slots, blockIdx.x, bh, slot);
     } else if (PERSIST) {
-        bh = blockIdx.x & 7;   // set per item below
+        bh = 0;   // set per item below
         slot = 0;
     } else {
         map_head_tile(blockIdx.x, p.total_wg, p.n_slots, bh, slot);
@@ -148,13 +149,17 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     const int Nq = sg.Nq, Nk = sg.Nk, off = Nk - Nq;
     const int nqt = VARLEN ? (Nq + BR - 1) / BR : p.n_qtiles;
     if (VARLEN && slot >= nqt) return;   // past the sequence's last query tile
-    // persistent schedule: this workgroup's XCD share x, its index l there,
-    // G workgroups per share, and its pairs l, l + G, ... of the share's
-    // U = heads_x * n_slots pairs (heads x, x + 8, ...)
+    // persistent schedule: this workgroup's XCD x, its index l there, G
+    // workgroups per XCD, and its pairs u0 + l, u0 + l + G, ... of the XCD's
+    // run [u0, u0 + U) of the T = BH * n_slots pairs (T < 2^31: fa_fwd
+    // bounds BH * (n_qtiles + 1))
     const int px = blockIdx.x & 7, pl = blockIdx.x >> 3, pG = p.total_wg >> 3;
     int n_items = (!SPLIT && p.paired && slot != nqt - 1 - slot) ? 2 : 1;
+    int pu0 = 0;
     if constexpr (PERSIST) {
-        const int U = ((p.BH - px + 7) >> 3) * p.n_slots;
+        const long long T = (long long)p.BH * p.n_slots;
+        pu0 = (int)(T * px / 8);
+        const int U = (int)(T * (px + 1) / 8) - pu0;
         n_items = pl < U ? 2 * ((U - pl + pG - 1) / pG) : 0;
     }
     // right bound: key <= query + offr; left bound (windows): key >= query + offl
@@ -224,9 +229,9 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // this item's query tile, and the next item's (-1: none)
     int qt, nxt_qt = -1;
     if constexpr (PERSIST) {
-        // item it: pair l + (it / 2) G of the share, its tile n-1-s, then s
-        const int u = pl + (it >> 1) * pG, hh = u / p.n_slots, s_ = u - hh * p.n_slots;
-        bh = 8 * hh + px;
+        // item it: pair u0 + l + (it / 2) G, its tile n-1-s, then s
+        const int u = pu0 + pl + (it >> 1) * pG, hh = u / p.n_slots, s_ = u - hh * p.n_slots;
+        bh = hh;
         qt = (it & 1) ? s_ : nqt - 1 - s_;
         sg.q_row0 = (size_t)bh * Nq;
         sg.k_row0 = (size_t)bh * Nk;
@@ -242,7 +247,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
                 nv_w = rv_w;
             } else {           // the next pair: another head, probably
                 const int u2 = u + pG, hh2 = u2 / p.n_slots, s2 = u2 - hh2 * p.n_slots;
-                const size_t bh2 = 8 * (size_t)hh2 + px;
+                const size_t bh2 = (size_t)hh2;
                 nxt_qt = nqt - 1 - s2;
                 nq_w = make_rsrc_words((const bf16*)p.q + bh2 * Nq * D, q_bytes);
                 nk_w = make_rsrc_words((const bf16*)p.k + bh2 * Nk * D, k_bytes);

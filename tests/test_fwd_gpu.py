@@ -157,8 +157,9 @@ def test_paired_query_tiles_sampled_heads(case):
 # ------------------------------------- persistent grid (causal d = 128, large)
 # With causal masking, d = 128, an even query-tile count and at least 1024
 # mirrored pairs of 128-row query tiles, the forward runs 512 persistent
-# workgroups, each taking pairs of the heads of one XCD share (heads = w mod 8)
-# and prefetching its next item across heads.  These shapes take that path
+# workgroups.  The pairs, head-major, are cut into eight equal runs, one per
+# XCD (workgroup w is on XCD w mod 8); each workgroup takes pairs of its run
+# and prefetches its next item across heads.  These shapes take that path
 # with a ragged tail and a head count that leaves the shares unequal, and with
 # Nq != Nk both ways.  Each sampled head is also run alone (one workgroup per
 # query tile, every key walk upwards): the query tiles of the upper half, the
@@ -198,6 +199,40 @@ def test_persistent_grid_sampled_heads_and_bitwise(case):
         assert torch.equal(fin, torch.isfinite(lseh[:up])), f"{case} head {bh}: empty rows differ"
         assert (lse1[:up][fin] - lseh[:up][fin]).abs().max().item() <= 1e-5 if fin.any() else True
         assert (o1[:up].float() - oh[:up].float()).abs().max().item() <= 2e-2
+
+
+# Fewer heads than XCDs, or a count that is not a multiple of eight: every
+# XCD still gets an eighth of the pairs, so runs start and end inside heads
+# and one head's pairs are served by several XCDs.  Rows are sampled per head
+# (the heads are too long for the whole-head oracle), and each head is also
+# run alone (fewer than 1024 pairs: one workgroup per query tile), whose
+# upper-half query tiles must be bitwise equal.
+PERSIST_FEW_HEADS = [
+    # B, H, N
+    (1, 3, 90000),     # 704 query tiles (16-row tail), 1056 pairs: runs of 132
+    (1, 2, 131000),    # 1024 query tiles, 1024 pairs: each head spans four runs
+]
+
+
+@pytest.mark.parametrize("case", PERSIST_FEW_HEADS, ids=lambda c: "-".join(map(str, c)))
+def test_persistent_grid_few_heads_sampled_rows_and_bitwise(case):
+    B, H, N = case
+    d = 128
+    n_qt = (N + 127) // 128
+    assert n_qt % 2 == 0 and B * H * (n_qt // 2) >= 1024 and (n_qt // 2) < 1024   # persistent; a lone head is not
+    banner(f"fwd persistent few heads {case}")
+    q, k, v = wl.make_inputs(B, H, N, N, d, "bf16", seed=970 + H)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = gpu_fwd(q, k, v, scale, True)
+    up = (n_qt // 2) * 128   # first row of the upper half's query tiles
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        rows = wl.sample_rows(N, 128, 9700 + bh)
+        o_ref, lse_ref = attention_forward_rows(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), scale, True, rows)
+        check_forward(to64(o[b, h, rows]), to64(lse[b, h, rows]), o_ref, lse_ref, "bf16", f"{case} head {bh}")
+        o1, lse1 = gpu_fwd(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], scale, True)
+        assert torch.equal(o1[0, 0, up:].cpu(), o[b, h, up:].cpu()), f"{case} head {bh}: O (upper tiles) differs from the lone head"
+        assert torch.equal(lse1[0, 0, up:].cpu(), lse[b, h, up:].cpu()), f"{case} head {bh}: LSE (upper tiles) differs"
 
 
 # ------------------------------------------------------------------ page pins
