@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdParams p) {
     // workgroup)
     int bh, slot;
     if (VARLEN) varlen_slot(p.vl, p.kv_slots, blockIdx.x, bh, slot);
-    else map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, slot);
+    else map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, slot, MASK == kMaskCausal && !p.kv_paired);
     // the (batch, head) pair's lengths and first rows (variable-length
     // batches: its own sequence's; a workgroup past its key tiles exits)
     SeqGeometry sg;
@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdParams p) {
     // with pairing its mirror j
     int bh, slot;
     if (VARLEN) varlen_slot(p.vl, p.q_slots, blockIdx.x, bh, slot);
-    else map_head_tile(blockIdx.x, p.BH * p.q_slots, p.q_slots, bh, slot);
+    else map_head_tile(blockIdx.x, p.BH * p.q_slots, p.q_slots, bh, slot, MASK == kMaskCausal && !p.q_paired);
     SeqGeometry sg;
     if constexpr (VARLEN) sg = seq_geometry(p.vl, bh);
     else sg = SeqGeometry{p.Nq, p.Nk, (size_t)bh * p.Nq, (size_t)bh * p.Nk};
@@ -654,7 +654,7 @@ __global__ void __launch_bounds__(256 * QSPLIT, (D == 64 || QSPLIT == 2) ? 2 : 1
     const int dq_qb = wave * DQB / NDB, dq_db = wave * DQB % NDB;   // its first dQ block
     int bh, slot;
     if (VARLEN) varlen_slot(p.vl, p.kv_slots, blockIdx.x, bh, slot);
-    else map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, slot);
+    else map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, slot, MASK == kMaskCausal && !p.kv_paired);
     SeqGeometry sg;
     if constexpr (VARLEN) sg = seq_geometry(p.vl, bh);
     else sg = SeqGeometry{p.Nq, p.Nk, (size_t)bh * p.Nq, (size_t)bh * p.Nk};

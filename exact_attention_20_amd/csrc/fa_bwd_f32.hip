@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(128) bwd_f32_dq_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hg = lane >> 5;
     int bh, qt;
-    map_head_tile(blockIdx.x, p.BH * p.q_slots, p.q_slots, bh, qt);
+    map_head_tile(blockIdx.x, p.BH * p.q_slots, p.q_slots, bh, qt, MASK == kMaskCausal);
     qt = p.q_slots - 1 - qt;   // the heaviest causal tiles first
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
     constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
@@ -177,7 +177,7 @@ __global__ void __launch_bounds__(128) bwd_f32_dkdv_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hg = lane >> 5;
     int bh, kt;
-    map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, kt);   // first key tiles see the most queries
+    map_head_tile(blockIdx.x, p.BH * p.kv_slots, p.kv_slots, bh, kt, MASK == kMaskCausal);   // first key tiles see the most queries
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
     constexpr bool kRight = MASK != kMaskNone, kLeft = MASK == kMaskWindow;
     const int offr = off + (MASK == kMaskWindow ? p.wr : 0);

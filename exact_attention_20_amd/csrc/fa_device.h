@@ -482,7 +482,27 @@ struct LinTileCopy {
 // tiles running alone (a greedy-dispatch model of one XCD gives a tail of
 // 10% of the run with one head at a time, none with two).  An odd last head
 // keeps its own order.
-__device__ __forceinline__ void map_head_tile(int w, int total, int n_tiles, int& bh, int& tile) {
+//
+// unequal: the tiles' work falls from index 0 (causal tiles, heaviest first,
+// not paired).  Unless every XCD's run is whole two-head groups (batch*head
+// count a multiple of 16), runs cut into such groups would give one XCD the
+// heavy tiles of a group and the next its light ones; then the XCDs take
+// equal runs of mirrored pairs instead (tiles j and n-1-j of a head: equal
+// causal work), head-major: an XCD's workgroups first take the heavy tile of
+// each pair of its run in order, then the light tiles in reverse order, so
+// the lightest tiles fill the end.  Needs an even tile count and a multiple
+// of 16 workgroups (whole pairs per XCD); otherwise the map above is kept.
+__device__ __forceinline__ void map_head_tile(int w, int total, int n_tiles, int& bh, int& tile,
+                                              bool unequal = false) {
+    if (unequal && (total & 15) == 0 && (n_tiles & 1) == 0 && (total >> 3) % (2 * n_tiles) != 0) {
+        const int per = total >> 3, half = per >> 1, l = w >> 3, np = n_tiles >> 1;
+        const bool heavy = l < half;
+        const int u = (w & 7) * half + (heavy ? l : per - 1 - l);   // pair, head-major
+        bh = u / np;
+        const int j = u - bh * np;
+        tile = heavy ? j : n_tiles - 1 - j;
+        return;
+    }
     int L = w;
     if ((total & 7) == 0) {
         const int per = total >> 3;

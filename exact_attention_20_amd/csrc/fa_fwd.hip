@@ -29,8 +29,8 @@ namespace fa {
 // Workgroup id -> (batch*head, query tile): XCD-grouped heads (see
 // map_head_tile); within a head the heaviest (last, for causal) query tile is
 // issued first so the short tiles fill the tail.
-__device__ __forceinline__ void map_workgroup(int w, int total, int n_qtiles, int& bh, int& qt) {
-    map_head_tile(w, total, n_qtiles, bh, qt);
+__device__ __forceinline__ void map_workgroup(int w, int total, int n_qtiles, int& bh, int& qt, bool causal) {
+    map_head_tile(w, total, n_qtiles, bh, qt, causal);
     qt = n_qtiles - 1 - qt;
 }
 
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         bh = 0;   // set per item below
         slot = 0;
     } else {
-        map_head_tile(blockIdx.x, p.total_wg, p.n_slots, bh, slot);
+        map_head_tile(blockIdx.x, p.total_wg, p.n_slots, bh, slot, MASK == kMaskCausal && !p.paired);
     }
     // the (batch, head) pair's lengths and first rows in the [rows, D] views
     SeqGeometry sg;
@@ -694,7 +694,7 @@ __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hg = lane >> 5;
     int bh, qt;
-    map_workgroup(blockIdx.x, p.total_wg, p.n_qtiles, bh, qt);
+    map_workgroup(blockIdx.x, p.total_wg, p.n_qtiles, bh, qt, MASK == kMaskCausal);
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
     const int q0 = qt * BR;
     const int qw = q0 + wave * 32;
