@@ -61,6 +61,7 @@ SMALL = [
     (1, 2, 200, 333, 128, False, None),
     (1, 1, 257, 257, 64, True, None),
     (1, 1, 1000, 1000, 128, True, None),    # many tiles each way
+    (1, 4, 500, 500, 64, True, None),       # 8 tiles per head, 32 workgroups: XCD runs of mirrored pairs
     (1, 2, 300, 300, 64, False, (16, 0)),
     (1, 2, 333, 333, 128, False, (100, 50)),
     (1, 1, 500, 200, 64, False, (31, 0)),   # leading rows and some keys see nothing

@@ -63,6 +63,33 @@ def test_backward_small_and_ragged(case, det):
     check_grad(to64(dv), rv, f"dv {case}")
 
 
+# Unpaired causal grids whose batch*head count is not a multiple of 16: both
+# kernels' workgroup maps give each XCD an equal run of mirrored tile pairs
+# (heavy tiles first, light ones in reverse).  Every head is checked.
+XCD_RUNS = [
+    # B, H, Nq, Nk, d
+    (1, 4, 2000, 2000, 128),      # 16 key and query tiles, ragged tail
+    (1, 6, 2048, 2048, 64),
+    (1, 4, 1500, 2048, 128),      # Nk > Nq: 12 query tiles, 16 key tiles
+]
+
+
+@pytest.mark.parametrize("det", MODES, ids=mode_id)
+@pytest.mark.parametrize("case", XCD_RUNS, ids=lambda c: "-".join(map(str, c)))
+def test_backward_xcd_pair_runs(case, det):
+    B, H, Nq, Nk, d = case
+    for n in ((Nq + 127) // 128, (Nk + 127) // 128):
+        assert n % 2 == 0 and (B * H * n) % 16 == 0 and (B * H * n // 8) % (2 * n) != 0   # the map's new branch
+    banner(f"bwd xcd pair runs {case} {mode_id(det)}")
+    q, k, v, do = wl.make_inputs(B, H, Nq, Nk, d, "bf16", seed=590 + Nq + Nk + d, with_do=True)
+    scale = 1.0 / np.sqrt(d)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, do, scale, True, det)
+    rq, rk, rv, *_ = attention_backward(to64(q), to64(k), to64(v), to64(do), scale, True)
+    check_grad(to64(dq), rq, f"dq {case}")
+    check_grad(to64(dk), rk, f"dk {case}")
+    check_grad(to64(dv), rv, f"dv {case}")
+
+
 # Large causal grids take the paired path in both backward kernels (a
 # workgroup runs key tile j then n-1-j, query tile n-1-j then j): odd tile
 # counts, ragged tails and Nq != Nk.

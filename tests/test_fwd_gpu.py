@@ -154,6 +154,37 @@ def test_paired_query_tiles_sampled_heads(case):
         check_forward(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, "bf16", f"{case} head {bh}")
 
 
+# ------------------------- XCD runs of mirrored pairs (unpaired causal grids)
+# When the batch*head count is not a multiple of 16, the workgroup map gives
+# each XCD an equal run of mirrored query-tile pairs (its heavy tiles first,
+# then the light ones in reverse) instead of cutting two-head groups between
+# XCDs.  These shapes take that map (an even tile count, a multiple of 16
+# workgroups, runs that are not whole two-head groups); every head is checked.
+XCD_RUNS = [
+    # B, H, Nq, Nk, d
+    (1, 4, 2000, 2000, 128),      # 16 query tiles, 80-row tail: runs of 4 pairs
+    (1, 6, 2048, 2048, 64),       # 96 workgroups, runs of 6 pairs
+    (1, 12, 1024, 1024, 128),     # 8 query tiles per head
+    (1, 4, 1500, 2048, 128),      # Nk > Nq (bottom-right causal alignment)
+]
+
+
+@pytest.mark.parametrize("case", XCD_RUNS, ids=lambda c: "-".join(map(str, c)))
+def test_xcd_pair_runs_whole_heads(case):
+    B, H, Nq, Nk, d = case
+    n_qt = (Nq + 127) // 128
+    total = B * H * n_qt
+    assert n_qt % 2 == 0 and total % 16 == 0 and (total // 8) % (2 * n_qt) != 0   # the map's new branch
+    banner(f"fwd xcd pair runs {case}")
+    q, k, v = wl.make_inputs(B, H, Nq, Nk, d, "bf16", seed=990 + Nq + Nk + d)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = gpu_fwd(q, k, v, scale, True)
+    for b in range(B):
+        for h in range(H):
+            o_ref, lse_ref = attention_forward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), scale, True)
+            check_forward(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, "bf16", f"{case} head {(b, h)}")
+
+
 # ------------------------------------- persistent grid (causal d = 128, large)
 # With causal masking, d = 128, an even query-tile count and at least 1024
 # mirrored pairs of 128-row query tiles, the forward runs 512 persistent
