@@ -133,13 +133,16 @@ def test_planted_jump_in_persistent_grid():
     """d = 128 causal over >= 1024 mirrored pairs of query tiles: the forward
     runs its persistent grid, where a workgroup's next item may belong to
     another head and has its first key tile prefetched during the current
-    item's last one.  A recomputation must leave the next items (the mirror
-    tile, and the next head of the same XCD share, h + 8) correct."""
+    item's last one.  A recomputation must leave the next items correct: the
+    mirror tile, and the workgroup's next pair.  Here 64 heads of 16 pairs
+    are cut into eight runs of 128 pairs (heads 8x .. 8x + 7 on XCD x) and a
+    workgroup takes pairs l and l + 64 of its run, so the next pair after one
+    in head h (h mod 8 < 4) is in head h + 4."""
     B, H, N, d = 1, 64, 4096, 128
-    assert (N // 128) % 2 == 0 and B * H * (N // 256) >= 1024
+    assert (N // 128) % 2 == 0 and B * H * (N // 256) == 1024
     banner(f"fwd planted jump persistent B{B} H{H} N{N} d{d}")
     q, k, v = wl.make_inputs(B, H, N, N, d, "bf16", seed=4551)
-    heads = [(0, 3), (0, 12), (0, 21), (0, 46)]   # shares 3, 4, 5, 6
+    heads = [(0, 3), (0, 10), (0, 17), (0, 40)]   # XCDs 0, 1, 2, 5; first pairs of their workgroups
     rows = []
     for i, (b, h) in enumerate(heads):
         rows.append((b, h, N - 1 - 41 * i))        # the last query tile: the first item of its pair
@@ -150,7 +153,7 @@ def test_planted_jump_in_persistent_grid():
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all(), "non-finite output"
-    after = [(0, h + 8) for (_, h) in heads if h + 8 < H]
+    after = [(0, h + 4) for (_, h) in heads]
     check_heads(q, k, v, o, lse, scale, True, heads + after + [(0, 0)], f"persistent A={A}")
 
 
