@@ -39,6 +39,8 @@ CASES = [
     (1, 2, 1, 70, 128, True, 5),        # one query row: more runs than key tiles
     (3, 2, 1, 2500, 64, True, 0),       # one query row, d = 64, automatic runs
     (1, 1, 1, 200, 128, False, 1),      # one query row, one run
+    (1, 2, 1, 0, 128, True, 0),         # one query row, no keys: O = 0, LSE = -inf
+    (2, 1, 1, 0, 64, False, 3),
 ]
 
 
