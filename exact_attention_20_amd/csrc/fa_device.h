@@ -1,6 +1,6 @@
 // Device-side building blocks shared by the forward and backward kernels:
-// vector types, the 32x32 MFMA wrappers, LDS tile swizzles, and the
-// register-level 4x8 bf16 transpose used to stage a tile key-major.
+// vector types, the 32x32 MFMA wrappers, buffer and LDS-direct copies, the
+// LDS tile layouts and their operand reads, and the workgroup maps.
 //
 // MFMA register layouts used throughout (CDNA3/CDNA4 32x32 shapes, wave64):
 //   A operand (M x K):  lane l holds row m = l % 32, k-group l / 32.
@@ -79,40 +79,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Byte offset of 16-byte chunk `chunk` of row `row` in a row-major LDS tile
-// whose rows are `row_bytes` long.  The chunk index is XOR-ed with the low
-// three bits of the row, so eight consecutive rows read at the same logical
-// chunk land in eight different bank groups (conflict-free ds_read_b128).
-// Rows shorter than 8 chunks XOR with fewer bits so the chunk stays in its row.
-template <uint32_t ROW_BYTES>
-__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
-    constexpr uint32_t kChunks = ROW_BYTES / 16;
-    constexpr uint32_t kMask = kChunks >= 8 ? 7u : kChunks - 1u;
-    static_assert(ROW_BYTES % 16 == 0 && kChunks >= 1, "rows are whole 16-byte chunks");
-    return row * ROW_BYTES + ((chunk ^ (row & kMask)) << 4);
-}
-
-// Position of index `i` inside its 16-group when a tile is stored
-// "k-permuted": bits 2 and 3 are swapped, so the 8 indices a 32x32x16 MFMA
-// lane-group consumes -- {4g..4g+3, 8+4g..8+4g+3} for g = 0, 1, which is the
-// order a 32x32 accumulator hands them out -- sit in 16 contiguous bytes.
-__device__ __forceinline__ uint32_t kperm(uint32_t i) {
-    return (i & ~12u) | ((i & 4u) << 1) | ((i & 8u) >> 1);
-}
-
-// Transpose four rows x eight bf16 columns held as four 16-byte vectors into
-// eight columns x four rows (each 8 bytes): out[c] = {r0[c], r1[c], r2[c], r3[c]}.
-__device__ __forceinline__ void transpose4x8(const u32x4 (&r)[4], u32x2 (&out)[8]) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        // low halves -> column 2p, high halves -> column 2p+1
-        out[2 * p][0] = __builtin_amdgcn_perm(r[1][p], r[0][p], 0x05040100u);
-        out[2 * p][1] = __builtin_amdgcn_perm(r[3][p], r[2][p], 0x05040100u);
-        out[2 * p + 1][0] = __builtin_amdgcn_perm(r[1][p], r[0][p], 0x07060302u);
-        out[2 * p + 1][1] = __builtin_amdgcn_perm(r[3][p], r[2][p], 0x07060302u);
-    }
-}
-
 __device__ __forceinline__ u32x4 ldg128(const void* p) { return *(const u32x4*)p; }
 
 // Raw buffer resource over `bytes` bytes at `base`.  Loads through it return
@@ -127,19 +93,13 @@ __device__ __forceinline__ u32x4 buf_load128(__amdgpu_buffer_rsrc_t r, uint32_t 
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// 16 bytes per lane from a buffer straight into LDS (no VGPRs): lane l's
-// data lands at lds_base + 16*l.  lds_base must be the same in every lane.
-__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff,
-                                               uint32_t soff) {
-    typedef __attribute__((address_space(3))) void lds_void_t;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, soff, 0, 0);
-}
-
-// The same 16-byte HBM -> LDS copy issued through inline asm, so the
-// compiler's memory-wait analysis does not see it: it would otherwise wait
-// for the copy before every LDS read and every barrier, since it cannot tell
-// which LDS buffer the copy fills.  Completion MUST be awaited explicitly
-// with vmem_wait_all() before any wave reads the destination.
+// A 16-byte-per-lane HBM -> LDS copy (buffer_load_dwordx4 ... lds: lane l's
+// data lands at the LDS address in M0 + 16*l, no VGPRs) issued through
+// inline asm, so the compiler's memory-wait analysis does not see it: with
+// the builtin form it would wait for the copy before every LDS read and
+// every barrier, since it cannot tell which LDS buffer the copy fills.
+// Completion MUST be awaited explicitly with vmem_wait_all() before any
+// wave reads the destination.
 //   rsrc: raw buffer descriptor words (wave-uniform);
 //   lds_addr: LDS byte address of lane 0's 16 bytes (wave-uniform).
 typedef int i32x4 __attribute__((ext_vector_type(4)));

@@ -14,9 +14,10 @@
 //   row max / row sum      : lane-local over the 16*NKB values, then one
 //                            exchange with the other 32-lane half.
 //   O^T[dv][q] += V^T P^T  : B = P^T straight from the S^T accumulator (no
-//                            LDS round trip), A = V^T rows from an LDS copy
-//                            of V stored dv-major with keys in the order the
-//                            accumulator hands them out (see kperm).
+//                            LDS round trip), A = V^T, read from the
+//                            untransposed V tile in LDS with the transposing
+//                            ds_read_b64_tr_b16, keys in the order the
+//                            accumulator hands them out.
 //   The rescale by alpha = 2^(m_old - m_new) is a per-lane scalar because a
 //   lane's O^T items all belong to its one query.
 // exp is computed as exp2 with scale*log2(e) folded into one FMA (§4 of the
