@@ -191,6 +191,24 @@ __device__ __forceinline__ void async_load_lds16_x4(i32x4 rsrc, uint32_t lds_add
 
 __device__ __forceinline__ void vmem_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Cache warm-up: one 4-byte load per lane from rsrc at voff + soff, written
+// to the 256-byte LDS area at sink_lds (lane l's bytes at sink_lds + 4*l;
+// nothing reads it), so that the 128-byte line holding it is in the L2 when
+// a copy asks for it later.  An LDS-destination load needs no VGPR to hold
+// its result while in flight.  It is counted by vmcnt like the copies, and
+// vector memory operations complete in issue order, so a wait for a copy
+// issued after it waits for it too: issue it where that wait comes late
+// anyway, and await it before the workgroup can end.  Out-of-range offsets
+// read nothing (the buffer range check).  Wait states as in async_load_lds16.
+__device__ __forceinline__ void l2_touch(i32x4 rsrc, uint32_t sink_lds, uint32_t voff, uint32_t soff) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dword %0, %1, %2 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(__builtin_amdgcn_readfirstlane(sink_lds))
+        : "memory");
+}
+
 // An empty statement that reads `x`.  The compiler's wait analysis does not
 // treat an explicit s_waitcnt as completing the loads it tracks, but it does
 // place its own wait before an instruction that reads their results and then

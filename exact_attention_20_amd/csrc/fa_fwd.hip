@@ -103,6 +103,7 @@ template <int D, int MASK, bool SPLIT, bool VARLEN = false, bool PERSIST = false
 __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(FwdParams p) {
     static_assert(SWEXP == 0 || SWEXP == 2 || SWEXP == 4 || SWEXP == 8, "one exponential in 2, 4 or 8");
     static_assert(!PERSIST || (!SPLIT && !VARLEN), "the persistent schedule is for whole fixed-length query tiles");
+    static_assert(!PERSIST || D == 128, "the persistent Q warm-up covers 128 rows of 256 bytes");
     constexpr int BR = 128, BC = 64;
     constexpr int NKK = D / 16;        // k-steps over d for S^T
     constexpr int NKB = BC / 32;       // 32-key blocks per tile
@@ -121,6 +122,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_BYTES];
     __shared__ int redo_flag[4];   // per wave: a row left the fast path's range
+    __shared__ __attribute__((aligned(16))) int l2_sink[64];   // destination of l2_touch (never read)
 
     // wave index through readfirstlane: everything derived from it (LDS
     // addresses, the per-wave causal limits) stays in scalar registers
@@ -318,6 +320,17 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         const bool has_next = i_t + 1 < ntiles || next_ntiles > 0;
         if (i_t + 1 < ntiles) load_tile(rev ? k0 - BC : k0 + BC, buf ^ 1);
         else if (has_next) load_tile_r(nk_w, nv_w, nxt_first * BC, buf ^ 1);
+        // Persistent schedule: the next item's Q tile is copied in only after
+        // this item's epilogue (its LDS buffer is the one this last tile
+        // reads, then the output staging), so its lines are brought into the
+        // L2 now, one line per lane (the 128 x 256-byte tile is 256 lines, 64
+        // per wave), while this tile computes; the end-of-tile wait below
+        // awaits these loads too, and the copy then hits the L2.  (A timing
+        // probe that skipped the later items' Q copies bounds the gain at
+        // 2.1% on the Llama-shaped workload; this measured +1.3% to +1.9%.)
+        if (PERSIST && i_t + 1 == ntiles && more)
+            l2_touch(nq_w, lds_address(l2_sink), (uint32_t)lane * 128 + (uint32_t)wave * 8192,
+                     (uint32_t)nxt_qt * BR * D * 2);
 
         if (k0 < kend_w && (!kLeft || k0 + BC > kbeg_w)) {
             // ---- S^T = K Q^T (fp32 accumulators) ----
