@@ -447,10 +447,16 @@ def train_step_timing(fa, wl, steps: int, warmup: int, window=None, w=None):
         bwd.ws = ws
         return bwd
 
+    # the inputs were just made on the host, so each call settles the clock
+    # first (settle_clock) as the timed workload does
     fwd()
+    settle_clock(fwd, min_ms=100.0)
     ms_f = time_launches(fwd, stream, steps, warmup)
-    ms_b = time_launches(bwd_fn(1), stream, steps, warmup)
-    ms_a = time_launches(bwd_fn(0), stream, steps, warmup)
+    bwd_det, bwd_atomic = bwd_fn(1), bwd_fn(0)
+    settle_clock(bwd_det, min_ms=100.0)
+    ms_b = time_launches(bwd_det, stream, steps, warmup)
+    settle_clock(bwd_atomic, min_ms=100.0)
+    ms_a = time_launches(bwd_atomic, stream, steps, warmup)
     causal = w.causal if window is None else False
     pairs = visible_pairs(w.Nq, w.Nk, causal, window) * w.B * w.H
     shape = w.describe() if window is None else w.describe().replace("causal", f"window {window}")
@@ -565,6 +571,7 @@ def bench_varlen(fa, wl, w, args) -> dict:
                 if st != 0:
                     raise fa.FAError(st, "fa_bwd_varlen")
 
+            settle_clock(bwd, min_ms=100.0)
             bwd_ms[det] = time_launches(bwd, stream, 20, 5)
             del ws
         result["backward"] = {"bwd_ms": round(bwd_ms[1], 5),
