@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
     // persistent schedule: this workgroup's XCD x, its index l there, G
     // workgroups per XCD, and its pairs u0 + l, u0 + l + G, ... of the XCD's
     // run [u0, u0 + U) of the T = BH * n_slots pairs (T < 2^31: fa_fwd
-    // bounds BH * (n_qtiles + 1))
+    // bounds B * H * (ceil(Nq / 64) + 1) by 2e9)
     const int px = blockIdx.x & 7, pl = blockIdx.x >> 3, pG = p.total_wg >> 3;
     int n_items = (!SPLIT && p.paired && slot != nqt - 1 - slot) ? 2 : 1;
     int pu0 = 0;
@@ -325,7 +325,8 @@ __global__ void __launch_bounds__(256, fwd_waves_per_simd<D>()) fwd_bf16_kernel(
         // reads, then the output staging), so its lines are brought into the
         // L2 now, one line per lane (the 128 x 256-byte tile is 256 lines, 64
         // per wave), while this tile computes; the end-of-tile wait below
-        // awaits these loads too, and the copy then hits the L2.  (A timing
+        // awaits these loads too (or, if the next item has no key tile, its
+        // prologue's wait does), and the copy then hits the L2.  (A timing
         // probe that skipped the later items' Q copies bounds the gain at
         // 2.1% on the Llama-shaped workload; this measured +1.3% to +1.9%.)
         if (PERSIST && i_t + 1 == ntiles && more)
